@@ -1,0 +1,35 @@
+"""Float64 CPU oracle for paged split-KV decode attention and its LSE merge.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke
+check in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py``
+may import or call anything in this package.  The GPU library never links,
+imports or falls back to it, and this package imports nothing from the GPU
+library: the two share only the seeded input generator, which holds none of
+the method's arithmetic.
+
+What it computes (KV-cache engineering page, section "Exact recent pages,
+compact older pages"): single-token decode attention over a request's whole
+key/value history, once in one pass, and once tile by tile where every tile
+yields its own normalised output and log-sum-exp and a merge reweights the
+tiles by exp(lse_t - max lse), divides by the summed weights and reports
+max + log(sum) as the merged log-sum-exp.  The merged result is softmax
+attention over the union of all keys.
+
+Every function here is pinned by ``tests/test_oracle.py`` against things
+other than itself: brute force with exact summation, library routines
+(torch's scaled-dot-product attention, scipy's logsumexp), closed forms,
+hand-derived golden fixtures and planted mistakes.
+"""
+
+from .attention import (  # noqa: F401
+    widen_bf16,
+    kv_head_of,
+    attend,
+    tile_bounds,
+    tile_partials,
+    merge,
+    decode_one_pass,
+    decode_tiled,
+    stress_partials,
+    union_attention,
+)

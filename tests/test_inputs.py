@@ -1,0 +1,119 @@
+"""The seeded input generator (CPU only): bf16 rounding, page tables, pool
+layout and determinism."""
+
+import json
+import os
+
+import numpy as np
+import torch
+
+from paged_kv_cache_10_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_bf16_rounding_golden():
+    with open(os.path.join(GOLDEN, "bf16_patterns.json")) as f:
+        g = json.load(f)
+    for src, dst in g["round"]:
+        x = np.array([int(src, 16)], dtype=np.uint32).view(np.float32)
+        assert int(I.bf16_bits(x)[0]) == int(dst, 16), src
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(1).standard_normal(200000).astype(np.float32)
+    x = np.concatenate([x, x * 1e-30, x * 1e30])
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(I.bf16_bits(x), t)
+
+
+def test_draws_are_deterministic_and_distinct():
+    w = I.workload("tiny", ctx_lens=[300])
+    k1, v1 = I.draw_kv(w, 0, 0)
+    k2, v2 = I.draw_kv(w, 0, 0)
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
+    assert not np.array_equal(k1, v1)
+    w2 = I.workload("tiny", ctx_lens=[300], num_layers=2)
+    k3, _ = I.draw_kv(w2, 1, 0)
+    assert not np.array_equal(k1, k3)
+
+
+def test_boost_count_and_factor():
+    w = I.workload("long262k", ctx_lens=[6400], num_layers=1)
+    idx = I.boost_positions(w, 0, 0, 2, 6400)
+    assert len(idx) == 64 and len(set(idx.tolist())) == 64
+    k, _ = I.draw_kv(w, 0, 0)
+    w0 = I.workload("long262k", ctx_lens=[6400], num_layers=1, boost_frac=0.0)
+    k0, _ = I.draw_kv(w0, 0, 0)
+    from oracle import widen_bf16
+    a, b = widen_bf16(k[2, idx]), widen_bf16(k0[2, idx])
+    np.testing.assert_array_equal(a, 4 * b)
+    rest = np.setdiff1d(np.arange(6400), idx)
+    np.testing.assert_array_equal(k[2, rest], k0[2, rest])
+
+
+def test_page_tables_are_a_permutation_with_sinks():
+    w = I.workload("mixed", num_layers=1)
+    t = I.draw_page_tables(w)
+    assert t.shape == (16, w.pt_stride) and t.dtype == np.int32
+    used = []
+    for b, n in enumerate(w.pages_per_req):
+        assert np.all(t[b, :n] >= 0) and np.all(t[b, n:] == -1)
+        assert t[b, 0] >= 0                               # sink page present
+        used += t[b, :n].tolist()
+    assert sorted(used) == list(range(w.num_pages))
+    w2 = I.workload("conc", num_layers=1)
+    t2 = I.draw_page_tables(w2)
+    u2 = t2[t2 >= 0]
+    assert len(u2) == 1984 and len(set(u2.tolist())) == 1984 and u2.max() < 2048
+
+
+def test_mixed_lengths_in_range():
+    w = I.workload("mixed")
+    assert len(w.ctx_lens) == 16
+    assert all(1024 <= c <= 131072 for c in w.ctx_lens)
+
+
+def test_pool_layout():
+    """K block token-major [64][D], V block dim-major [D][64], at the page
+    the table names, in the layer's slot of that page."""
+    w = I.Workload("t", seed=3, ctx_lens=[100, 70], num_layers=2, tile_tokens=64,
+                   num_q_heads=4, num_kv_heads=2, head_dim=8)
+    t = I.draw_page_tables(w)
+    pool, kv = I.host_pool(w, t, fill=I.BF16_QNAN)
+    assert pool.shape == (w.num_pages, 2, 2, 2, 64 * 8)
+    for (layer, b), (k, v) in kv.items():
+        for g in range(2):
+            for j in [0, 1, 63, 64, w.ctx_lens[b] - 1]:
+                if j >= w.ctx_lens[b]:
+                    continue
+                p = t[b, j // 64]
+                jj = j % 64
+                for d in [0, 3, 7]:
+                    assert pool[p, layer, 0, g, jj * 8 + d] == k[g, j, d]
+                    assert pool[p, layer, 1, g, d * 64 + jj] == v[g, j, d]
+    # padding past ctx in the last page keeps the poison pattern
+    p = t[0, 1]
+    assert pool[p, 0, 0, 0, (100 - 64) * 8] == I.BF16_QNAN
+
+
+def test_device_scatter_matches_host_layout():
+    """The torch scatter used for full-size workloads writes the same layout."""
+    w = I.Workload("t", seed=4, ctx_lens=[130, 64], num_layers=2, tile_tokens=64,
+                   num_q_heads=4, num_kv_heads=2, head_dim=8)
+    t = I.draw_page_tables(w)
+    pool_h, kv = I.host_pool(w, t, fill=0)
+    pool_d = torch.zeros(pool_h.shape, dtype=torch.int16)
+    for (layer, b), (k, v) in kv.items():
+        kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16)
+        vt = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16)
+        I.device_scatter(pool_d, w, layer, b, t[b], kt, vt)
+    np.testing.assert_array_equal(pool_d.numpy().view(np.uint16), pool_h)
+
+
+def test_stress_draws_forced_rows():
+    d = I.stress_draws(batch=2, heads=3, tiles=32, keys=2, dim=4)
+    assert d["empty"][0, 0].all()
+    assert (~d["empty"][0, 1]).sum() == 1
+    assert d["target_lse"].min() >= -40 and d["target_lse"].max() <= 40
