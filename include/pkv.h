@@ -1,0 +1,193 @@
+/*
+ * pkv.h - paged KV decode attention on MI355X (gfx950): the C ABI.
+ *
+ * What it computes.  Exact single-token decode attention over a request's
+ * whole paged key/value history (KV-cache engineering page, section "Costing
+ * the bus before changing anything": every new token reads every byte of
+ * history).  The history is cut into tiles; each tile yields its normalised
+ * output and its log-sum-exp, and an FP32 merge weights tile t by
+ * exp(lse_t - max lse), sums, divides by the summed weights and reports
+ * max + log(sum) as the merged log-sum-exp: softmax over the union of the
+ * keys (same page, section "Exact recent pages, compact older pages").
+ *
+ * Conventions for every entry point.
+ *   - Return value: PKV_OK (0) or a negative PKV_ERR_* code.  No exception
+ *     crosses the ABI.  pkv_last_error() gives a message for the calling
+ *     thread that names the offending argument and the setting to change.
+ *   - Validation is on the host and synchronous, before any device work.
+ *     Kernels never check, never fault on a validated call and never sync.
+ *   - Device pointers and streams belong to the caller.  The library never
+ *     allocates device memory.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream); every kernel of a call is queued on it
+ *     in order and the host does not wait for it.
+ *   - bf16 means IEEE binary32's upper 16 bits; all outputs are FP32.
+ *   - The log-sum-exp is natural-log and includes the softmax scale:
+ *     lse = log sum_j exp(scale * q.k_j).
+ *
+ * Arena layout (one device allocation shared by every layer; GPU memory
+ * management page, "Pages held by right, borrowed or free").  A physical
+ * page holds page_tokens (64) consecutive tokens of one request for every
+ * layer:
+ *     arena[page][layer][K|V][kv_head][...]        (bf16)
+ *     K block: token-major [64][head_dim]   (row = one token's key)
+ *     V block: dim-major   [head_dim][64]   (row = one channel over 64 tokens)
+ * so one (page, layer) is 2 * Hkv * 64 * head_dim * 2 bytes (256 KiB at
+ * Hkv = 4, head_dim = 256) and one page is num_layers times that.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,      /* a null pointer, a negative size, an out-of-range index */
+  PKV_ERR_AUTO_SIZE_REFUSED = -2, /* arena_bytes == 0: the pool size must be explicit */
+  PKV_ERR_GEOMETRY = -3,         /* a head shape the kernels are not built for */
+  PKV_ERR_WORKSPACE = -4,        /* workspace missing or smaller than pkv_decode_workspace_bytes */
+  PKV_ERR_PAGE_TABLE = -5,       /* a page-table row the pool cannot serve */
+  PKV_ERR_LAUNCH = -6,           /* the HIP runtime refused a launch */
+  PKV_ERR_DEVICE = -7            /* a HIP runtime call (copy, device query) failed */
+};
+
+/* Geometry of the arena.  The kernels are built for head_dim = 256,
+ * page_tokens = 64 and a query group (num_q_heads / num_kv_heads) of 1..16;
+ * other shapes are refused with PKV_ERR_GEOMETRY. */
+typedef struct pkv_geom {
+  int32_t num_layers;    /* dense layers sharing the arena, >= 1            */
+  int32_t num_kv_heads;  /* KV heads per layer, >= 1                        */
+  int32_t head_dim;      /* channels per head: 256                          */
+  int32_t page_tokens;   /* tokens per page: 64                             */
+} pkv_geom;
+
+typedef struct pkv_pool pkv_pool;   /* opaque host-side handle */
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library ABI version (PKV_ABI_VERSION). */
+#define PKV_ABI_VERSION 1
+int32_t pkv_abi_version(void);
+
+/* Bytes of one physical page (all layers) for `geom`. */
+int pkv_page_bytes(const pkv_geom* geom, uint64_t* page_bytes_out);
+
+/* ---------------------------------------------------------------- pool --
+ * Wrap a caller-owned device arena of an explicit size as a page pool
+ * (GPU memory management page, "A host pool that explains its own size":
+ * an automatic size is refused outright).
+ *   dev_arena    device pointer, 256-byte aligned, caller keeps it alive
+ *                past pkv_pool_destroy.
+ *   arena_bytes  explicit size: 0 -> PKV_ERR_AUTO_SIZE_REFUSED; it must be
+ *                a whole number of pages (pkv_page_bytes), else
+ *                PKV_ERR_INVALID_ARG with the nearest valid sizes named.
+ * num_pages = arena_bytes / page_bytes.  Physical page ids are 0..num_pages-1.
+ * The handle owns host memory only; pkv_pool_destroy frees it and never
+ * waits on the device. */
+int pkv_pool_create(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes,
+                    pkv_pool** pool_out);
+int pkv_pool_info(const pkv_pool* pool, int64_t* num_pages, uint64_t* page_bytes,
+                  void** dev_arena);
+int pkv_pool_destroy(pkv_pool* pool);
+
+/* ---------------------------------------------------------- page table --
+ * A page table is int32 [batch][pt_stride] in row-major order: entry i of
+ * row b is the physical page holding tokens [64 i, 64 i + 64) of request b.
+ * ctx_lens is int32 [batch]: request b's history is tokens [0, ctx_lens[b]).
+ * A row is served only if (checked here, on the host):
+ *   - 0 <= ctx_lens[b] <= 64 * pt_stride;
+ *   - its first ceil(ctx_lens[b] / 64) entries are pages in [0, num_pages);
+ *     entry 0 is the request's attention-sink page, so a row with ctx > 0
+ *     always names it (GPU memory management page, "Pages held by right,
+ *     borrowed or free": the sink is always kept);
+ *   - every later entry is -1 (padding is contiguous);
+ *   - no physical page appears twice in the whole table.
+ * pkv_page_table_validate only checks.  pkv_page_table_write checks, then
+ * copies both host arrays to the caller's device arrays on `stream` and
+ * waits for that copy, so the host arrays may be reused on return (a table
+ * changes between decode steps, not inside one). */
+int pkv_page_table_validate(const pkv_pool* pool, const int32_t* host_table,
+                            const int32_t* host_ctx_lens, int32_t batch, int32_t pt_stride);
+int pkv_page_table_write(const pkv_pool* pool, const int32_t* host_table,
+                         const int32_t* host_ctx_lens, int32_t batch, int32_t pt_stride,
+                         int32_t* dev_table, int32_t* dev_ctx_lens, void* stream);
+
+/* -------------------------------------------------------------- decode --
+ * Per-tile partials of decode attention for one layer.
+ *
+ * Tiles are tile_tokens long and start at logical token 0: tile t of
+ * request b covers tokens [t T, min((t+1) T, ctx_b)).  One call covers the
+ * token window [token_begin, token_begin + token_count); both are
+ * multiples of tile_tokens, and the window writes slots
+ * [token_begin / T, (token_begin + token_count) / T) of every row.  A tile
+ * with no token of the request (ctx_b <= t T) is written as out = 0,
+ * lse = -inf.  One call over the whole history (token_begin = 0) and
+ * several calls over consecutive windows (staged tiles) write bit-identical
+ * partials: the arithmetic of a tile depends only on the tile's own keys.
+ *
+ *   pool, layer      arena and layer 0..num_layers-1.
+ *   q                device bf16 [batch][num_q_heads][head_dim] of this layer.
+ *   dev_table        device int32 rows as above; entry i of a row is the
+ *                    page of logical page (token_begin / 64 + i), so a
+ *                    staged call may pass the full table offset by
+ *                    token_begin / 64 entries, or a staging table.
+ *                    pt_stride >= token_count / 64 is required.  An entry
+ *                    outside [0, num_pages) is never dereferenced: its
+ *                    tokens are skipped (validated tables have none).
+ *   dev_ctx_lens     device int32 [batch], whole-history lengths.
+ *   tile_tokens      multiple of 64.
+ *   scale            softmax scale (1/sqrt(head_dim) for standard attention).
+ *   part_out         device FP32 [batch][num_q_heads][num_slots][head_dim].
+ *   part_lse         device FP32 [batch][num_q_heads][num_slots].
+ *   workspace        device scratch of at least pkv_decode_workspace_bytes
+ *                    (may be NULL when that is 0); contents need no init
+ *                    and are dead after the stream reaches the call's end.
+ *   opts             NULL for defaults (see pkv_decode_opts).
+ */
+typedef struct pkv_decode_opts {
+  int32_t kernel;        /* 0 default, 1 VALU (fdot2 + FP32 FMA), 2 MFMA (16x16x32 bf16) */
+  int32_t split_tokens;  /* 0 default; else tokens per work-group, a multiple of 64 dividing
+                            tile_tokens.  The split is a pure function of these options and
+                            tile_tokens, never of batch, lengths or the device, so staged and
+                            resident calls with the same options agree bit for bit. */
+} pkv_decode_opts;
+
+int pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                               int32_t token_count, int32_t tile_tokens,
+                               const pkv_decode_opts* opts, uint64_t* bytes_out);
+
+int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
+                         const int32_t* dev_table, int32_t pt_stride,
+                         const int32_t* dev_ctx_lens, int32_t batch, int32_t num_q_heads,
+                         int32_t token_begin, int32_t token_count, int32_t tile_tokens,
+                         float scale, float* part_out, float* part_lse, int32_t num_slots,
+                         void* workspace, uint64_t workspace_bytes,
+                         const pkv_decode_opts* opts, void* stream);
+
+/* --------------------------------------------------------------- merge --
+ * FP32 log-sum-exp merge of the partials of each row (KV-cache engineering
+ * page, section "Exact recent pages, compact older pages").  For row r,
+ * with M = max_t lse[r][t]:
+ *   M = -inf (every slot empty) -> out[r] = 0, lse[r] = -inf;
+ *   else w_t = exp(lse[r][t] - M), W = sum_t w_t,
+ *        out[r] = sum_t w_t part_out[r][t] / W, lse[r] = M + log W.
+ * Slots with lse = -inf add nothing (their part_out is never read into the
+ * sums), and the sums run over t in increasing order, so inserting empty
+ * slots leaves the result bit-identical and a single slot merges to itself.
+ *   part_out [rows][num_slots][head_dim], part_lse [rows][num_slots] (rows =
+ *   batch * num_q_heads), out [rows][head_dim], lse [rows]; all FP32 device.
+ * head_dim must be 256.  num_slots >= 1. */
+int pkv_merge_partials(const float* part_out, const float* part_lse, int32_t rows,
+                       int32_t num_slots, int32_t head_dim, float* out, float* lse,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,299 @@
+// Split-KV paged decode attention on the matrix cores (gfx950,
+// v_mfma_f32_16x16x32_bf16).
+//
+// One work-group (4 waves) owns one split of `split_tokens` tokens of one
+// request for one KV head; the KV head's query group (G <= 16 heads, padded
+// with zero rows to 16) is staged in LDS once.  Each wave takes every 4th
+// page of the split and keeps its own running max / sum; the four waves meet
+// in LDS at the end, in a fixed order.
+//
+// Per 32-token chunk of a page, in one wave:
+//   QK  S[token][head] = K[16 tokens x 256] . Q^T[256 x 16 heads], two MFMA
+//       tiles of 16 tokens x 8 steps of 32 channels.  Tile rows are assigned
+//       so that lane l ends up with the scores of tokens 8(l/16) .. +7 of
+//       head l%16, exactly the operand layout PV needs next.
+//   softmax  base-2 running max m and per-lane partial sum l in FP32; the
+//       chunk max meets across the 4 lanes of a head by two xor-shuffles.
+//   PV  O^T[channel][head] += V^T[16 channels x 32 tokens] . P^T[32 x 16].
+//       V blocks are stored dim-major, so the V^T operand is one contiguous
+//       16-byte load per lane.  P is split as p = hi + lo with hi, lo bf16
+//       (both round to nearest), two MFMAs per tile, so the product keeps
+//       ~2^-17 relative accuracy instead of bf16's 2^-9.
+// K/V loads of the next chunk are issued while the current chunk computes.
+//
+// Padding (tokens at or past the length, or pages whose id is out of range)
+// scores -inf and its V values are zeroed before the MFMA, so NaN padding
+// never reaches the sums.
+#include "device.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQPad = kHeadDim + 8;        // LDS row pitch of Q (bf16), breaks bank aliasing
+
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Zero bf16 element e of an 8-element operand when !keep[e].
+__device__ __forceinline__ uint4 mask_pairs(uint4 u, int live) {
+  // live = number of leading elements kept (0..8)
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (2 * i < live) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (2 * i + 1 < live) ? 0xffff0000u : 0u;
+    w[i] &= (lo | hi);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+struct Chunk {
+  const uint16_t* k;     // K block of the page (token-major)
+  const uint16_t* v;     // V block of the page (dim-major)
+  int base;              // first token of the chunk within the page (0 or 32)
+  int live;              // tokens of the chunk that exist (0..32)
+};
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int D = kHeadDim;
+  constexpr int PT = kPageTokens;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15;        // head column of every MFMA tile
+  const int q = lane >> 4;        // k-group of operands / row group of results
+
+  const int win_end = a.token_begin + a.token_count;
+  const int ctx = max(0, min(a.ctx_lens[b], win_end));
+  const int t0 = a.token_begin + split * a.split_tokens;
+  const int t1 = min(t0 + a.split_tokens, ctx);
+  const int slot = a.out_slot0 + split;
+  const int64_t row0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
+
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[16 * kQPad];
+  __shared__ float acc_lds[kWaves][G][D];
+  __shared__ float m_lds[kWaves][16];
+  __shared__ float l_lds[kWaves][16];
+
+  // ---- stage the query group (zero rows past G)
+  for (int i = tid; i < 16 * (D / 8); i += kThreads) {
+    const int h = i / (D / 8);
+    const int c8 = i % (D / 8);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < G) v = reinterpret_cast<const uint4*>(a.q + (row0 + h) * D)[c8];
+    *reinterpret_cast<uint4*>(&q_lds[h * kQPad + 8 * c8]) = v;
+  }
+  __syncthreads();
+
+  bf16x8_t qb[8];   // B operand of QK: head n, channels 32kb + 8q .. +7
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+    qb[kb] = as_bf16x8(*reinterpret_cast<const uint4*>(&q_lds[n * kQPad + 32 * kb + 8 * q]));
+
+  // rows of the two QK tiles: tile row r of tile t holds token 8(r/4) + 4t + r%4
+  const int krow0 = 8 * (n >> 2) + (n & 3);
+  const int krow1 = krow0 + 4;
+
+  float m = -INFINITY;   // running max of head n (base 2), same in the 4 lanes of a head
+  float lsum = 0.f;      // this lane's share of the running sum
+  f32x4_t acc[16];       // O^T tile db: channels 16db + 4q + i, head n
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* layer_base = a.arena + a.layer_off;
+  const int32_t* trow = a.table + (int64_t)b * a.pt_stride;
+  const int first_page = (t0 - a.token_begin) / PT;
+  const int n_pages = (t1 > t0) ? (t1 - t0 + PT - 1) / PT : 0;
+  // this wave's pages: w, w + 4, ... ; two chunks each
+  const int my_pages = (n_pages > w) ? (n_pages - w + kWaves - 1) / kWaves : 0;
+  const int n_chunks = 2 * my_pages;
+
+  auto chunk_at = [&](int ci) {
+    const int pi = w + kWaves * (ci >> 1);
+    const int tok = t0 + pi * PT;
+    int phys = trow[first_page + pi];
+    int valid = min(PT, t1 - tok);
+    if (phys < 0 || phys >= a.num_pages) { phys = 0; valid = 0; }   // read page 0, mask all
+    const uint16_t* page = layer_base + (int64_t)phys * a.page_elems;
+    Chunk c;
+    c.k = page + (int64_t)g * PT * D;
+    c.v = page + (int64_t)(a.num_kv_heads + g) * PT * D;
+    c.base = 32 * (ci & 1);
+    c.live = max(0, min(32, valid - c.base));
+    return c;
+  };
+
+  uint4 kreg[2][8];     // [tile][kb]
+  uint4 vreg[16];       // [db]
+  auto load_k = [&](const Chunk& c) {
+    const uint16_t* r0 = c.k + (c.base + krow0) * D + 8 * q;
+    const uint16_t* r1 = c.k + (c.base + krow1) * D + 8 * q;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      kreg[0][kb] = *reinterpret_cast<const uint4*>(r0 + 32 * kb);
+      kreg[1][kb] = *reinterpret_cast<const uint4*>(r1 + 32 * kb);
+    }
+  };
+  auto load_v = [&](const Chunk& c) {
+    const uint16_t* p = c.v + n * PT + c.base + 8 * q;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) vreg[db] = *reinterpret_cast<const uint4*>(p + 16 * db * PT);
+  };
+
+  Chunk cur;
+  if (n_chunks > 0) {
+    cur = chunk_at(0);
+    load_k(cur);
+    load_v(cur);
+  }
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    // ---- QK
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      s0 = mfma(as_bf16x8(kreg[0][kb]), qb[kb], s0);
+      s1 = mfma(as_bf16x8(kreg[1][kb]), qb[kb], s1);
+    }
+    Chunk nxt;
+    const bool more = ci + 1 < n_chunks;
+    if (more) {
+      nxt = chunk_at(ci + 1);
+      load_k(nxt);
+    }
+
+    // ---- online softmax; lane holds tokens 8q + e, e = 0..7, of head n
+    float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s[e] = (8 * q + e < cur.live) ? s[e] * a.scale_log2 : -INFINITY;
+      cmax = fmaxf(cmax, s[e]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float mn = fmaxf(m, cmax);
+    const float mref = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    m = mn;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(s[e] - mref);
+      ps += p[e];
+    }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      acc[db][0] *= alpha;
+      acc[db][1] *= alpha;
+      acc[db][2] *= alpha;
+      acc[db][3] *= alpha;
+    }
+    bf16x8_t phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 h = (__bf16)p[e];
+      phi[e] = h;
+      plo[e] = (__bf16)(p[e] - (float)h);
+    }
+
+    // ---- PV
+    const int vlive = max(0, min(8, cur.live - 8 * q));
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      uint4 vv = vreg[db];
+      if (cur.live < 32) vv = mask_pairs(vv, vlive);
+      const bf16x8_t va = as_bf16x8(vv);
+      acc[db] = mfma(va, phi, acc[db]);
+      acc[db] = mfma(va, plo, acc[db]);
+    }
+    if (more) {
+      load_v(nxt);
+      cur = nxt;
+    }
+  }
+
+  // ---- this wave's (m, l, acc) into LDS
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (q == 0) {
+    m_lds[w][n] = m;
+    l_lds[w][n] = lsum;
+  }
+  if (n < G) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_lds[w][n][16 * db + 4 * q + i] = acc[db][i];
+  }
+  __syncthreads();
+
+  // ---- fixed-order merge of the 4 waves; thread tid owns channel tid
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_lds[v][h]);
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float f = fast_exp2(m_lds[v][h] - M);     // 0 for a wave with no keys
+        if (f != 0.f) {
+          L = fmaf(f, l_lds[v][h], L);
+          o = fmaf(f, acc_lds[v][h][tid], o);
+        }
+      }
+    }
+    const bool live = L > 0.f;
+    a.out_o[((row0 + h) * a.out_slots + slot) * D + tid] = live ? o / L : 0.f;
+    if (tid == 0)
+      a.out_lse[(row0 + h) * a.out_slots + slot] = live ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, int batch, hipStream_t stream) {
+  const int n_split = a.token_count / a.split_tokens;
+  dim3 grid(n_split, a.num_kv_heads, batch);
+  hipLaunchKernelGGL(decode_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int group, hipStream_t stream) {
+  if (batch <= 0 || a.token_count <= 0) return hipSuccess;
+  switch (group) {
+    case 1: return launch_g<1>(a, batch, stream);
+    case 2: return launch_g<2>(a, batch, stream);
+    case 3: return launch_g<3>(a, batch, stream);
+    case 4: return launch_g<4>(a, batch, stream);
+    case 5: return launch_g<5>(a, batch, stream);
+    case 6: return launch_g<6>(a, batch, stream);
+    case 7: return launch_g<7>(a, batch, stream);
+    case 8: return launch_g<8>(a, batch, stream);
+    case 12: return launch_g<12>(a, batch, stream);
+    case 16: return launch_g<16>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

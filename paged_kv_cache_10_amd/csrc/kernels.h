@@ -1,0 +1,37 @@
+// Host-side launchers of the gfx950 kernels (internal to libpkv).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+
+namespace pkv {
+
+// Segmented FP32 log-sum-exp merge: output slot j of a row merges input
+// slots [j * group, min((j + 1) * group, in_slots)) of the same row.
+struct MergeArgs {
+  const float* in_o;     // [rows][in_slots][256]
+  const float* in_lse;   // [rows][in_slots]
+  int32_t in_slots;
+  int32_t group;
+  float* out_o;          // [rows][out_slots][256]
+  float* out_lse;        // [rows][out_slots]
+  int32_t out_slots;
+  int32_t out_slot0;     // output slot of j = 0
+  int32_t n_out;         // output slots written per row
+};
+
+hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t stream);
+
+// Split-KV decode: one work-group per (split, kv head, request) writes the
+// normalised output and log-sum-exp of its split for the kv head's query
+// group.  `group` = num_q_heads / num_kv_heads.
+hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int group, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int group, hipStream_t stream);
+
+// Largest query group each kernel supports.
+constexpr int kValuMaxGroup = 8;
+constexpr int kMfmaMaxGroup = 16;
+
+}  // namespace pkv

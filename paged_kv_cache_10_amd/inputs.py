@@ -193,16 +193,20 @@ def draw_kv(w, layer, b):
     return bf16_bits(k), bf16_bits(v)
 
 
-def draw_page_tables(w):
-    """int32 page tables [B, pt_stride]: a seeded permutation of the arena's
+def draw_page_tables(w, width=None):
+    """int32 page tables [B, width]: a seeded permutation of the arena's
     pages, request 0 taking the first ceil(ctx_0/64) entries, request 1 the
-    next, and so on; unused entries are -1.  Row b's entry 0 is its sink page."""
+    next, and so on; unused entries are -1.  Row b's entry 0 is its sink page.
+    width defaults to w.pt_stride (the longest request's page count)."""
     P = w.num_pages
     need = sum(w.pages_per_req)
     if need > P:
         raise ValueError(f"workload needs {need} pages, arena has {P}")
+    width = w.pt_stride if width is None else width
+    if width < w.pt_stride:
+        raise ValueError(f"width {width} < {w.pt_stride} pages of the longest request")
     perm = rng(w.seed, T_TABLE).permutation(P).astype(np.int32)
-    table = np.full((w.batch, w.pt_stride), -1, dtype=np.int32)
+    table = np.full((w.batch, width), -1, dtype=np.int32)
     o = 0
     for b, n in enumerate(w.pages_per_req):
         table[b, :n] = perm[o:o + n]
@@ -284,8 +288,8 @@ def device_q(w, layer, device):
 
 def device_scatter(pool, w, layer, b, table_row, k, v, pad_value=0):
     """Write logical K, V (torch bf16 [Hkv, ctx, D]) of one request into the
-    arena `pool` (torch int16/uint16-sized tensor viewable as
-    [P, L, 2, Hkv, 64*D]) at the pages of `table_row`."""
+    arena `pool` (a contiguous torch int16 tensor of P pages, any shape) at
+    the pages of `table_row`."""
     import torch
     Hkv, ctx, D = k.shape
     PT = w.page_tokens
@@ -293,7 +297,7 @@ def device_scatter(pool, w, layer, b, table_row, k, v, pad_value=0):
     if n == 0:
         return
     pages = torch.as_tensor(np.asarray(table_row[:n], dtype=np.int64), device=pool.device)
-    p5 = pool.view(torch.int16).view(pool.shape[0], w.num_layers, 2, Hkv, PT * D)
+    p5 = pool.view(torch.int16).reshape(-1).view(-1, w.num_layers, 2, Hkv, PT * D)
     def pad(x):
         if ctx == n * PT:
             return x

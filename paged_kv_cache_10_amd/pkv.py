@@ -1,0 +1,242 @@
+"""Thin Python binding of libpkv (include/pkv.h), one function per entry point.
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+layout, their pointers and the current HIP stream are passed to the C ABI,
+and a non-zero return raises PkvError with the library's message.  Every
+step of the computation runs in the library's kernels; there is no fallback:
+if libpkv.so is missing, lib() raises.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK = 0
+ERRORS = {
+    -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_AUTO_SIZE_REFUSED", -3: "PKV_ERR_GEOMETRY",
+    -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_PAGE_TABLE", -6: "PKV_ERR_LAUNCH", -7: "PKV_ERR_DEVICE",
+}
+KERNELS = {"default": 0, "valu": 1, "mfma": 2}
+
+# every symbol include/pkv.h declares
+EXPORTS = [
+    "pkv_last_error", "pkv_abi_version", "pkv_page_bytes", "pkv_pool_create", "pkv_pool_info",
+    "pkv_pool_destroy", "pkv_page_table_validate", "pkv_page_table_write",
+    "pkv_decode_workspace_bytes", "pkv_decode_attention", "pkv_merge_partials",
+]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32)]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32)]
+
+
+_lib = None
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+U64 = ctypes.c_uint64
+I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def lib():
+    """Load libpkv.so once; raise if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_10_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pkv_last_error.restype = ctypes.c_char_p
+        L.pkv_last_error.argtypes = []
+        L.pkv_abi_version.restype = I32
+        L.pkv_abi_version.argtypes = []
+        L.pkv_page_bytes.argtypes = [ctypes.POINTER(Geom), ctypes.POINTER(U64)]
+        L.pkv_pool_create.argtypes = [ctypes.POINTER(Geom), P, U64, ctypes.POINTER(P)]
+        L.pkv_pool_info.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(U64),
+                                    ctypes.POINTER(P)]
+        L.pkv_pool_destroy.argtypes = [P]
+        L.pkv_page_table_validate.argtypes = [P, I32P, I32P, I32, I32]
+        L.pkv_page_table_write.argtypes = [P, I32P, I32P, I32, I32, P, P, P]
+        L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32,
+                                                 ctypes.POINTER(DecodeOpts), ctypes.POINTER(U64)]
+        L.pkv_decode_attention.argtypes = [P, I32, P, P, I32, P, I32, I32, I32, I32, I32,
+                                           ctypes.c_float, P, P, I32, P, U64,
+                                           ctypes.POINTER(DecodeOpts), P]
+        L.pkv_merge_partials.argtypes = [P, P, I32, I32, I32, P, P, P]
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != PKV_OK:
+        raise PkvError(rc, lib().pkv_last_error().decode())
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t, dtype=None, name="tensor", need_cuda=True):
+    if t is None:
+        return None
+    if need_cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, need {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _i32_array(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(I32P)
+
+
+def _opts(kernel, split_tokens):
+    if kernel in (0, 0.0, None):
+        k = 0
+    else:
+        k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    return DecodeOpts(k, int(split_tokens or 0))
+
+
+def abi_version():
+    return lib().pkv_abi_version()
+
+
+def page_bytes(num_layers, num_kv_heads, head_dim=256, page_tokens=64):
+    out = U64()
+    _check(lib().pkv_page_bytes(ctypes.byref(Geom(num_layers, num_kv_heads, head_dim, page_tokens)),
+                                ctypes.byref(out)))
+    return out.value
+
+
+class Pool:
+    """A page pool over a caller-owned arena (any device tensor; its bytes are
+    the arena).  `arena_bytes` defaults to the tensor's size; 0 is refused."""
+
+    def __init__(self, arena, num_layers, num_kv_heads, head_dim=256, page_tokens=64,
+                 arena_bytes=None):
+        self.arena = arena                     # keeps the memory alive
+        self.geom = Geom(num_layers, num_kv_heads, head_dim, page_tokens)
+        nbytes = arena.numel() * arena.element_size() if arena_bytes is None else int(arena_bytes)
+        h = P()
+        ptr = arena.data_ptr()
+        _check(lib().pkv_pool_create(ctypes.byref(self.geom), ptr, nbytes, ctypes.byref(h)))
+        self.handle = h
+        n = ctypes.c_int64()
+        pb = U64()
+        _check(lib().pkv_pool_info(h, ctypes.byref(n), ctypes.byref(pb), None))
+        self.num_pages = n.value
+        self.page_bytes = pb.value
+        self.num_layers = num_layers
+        self.num_kv_heads = num_kv_heads
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().pkv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def page_table_validate(pool, table, ctx_lens):
+    """Host-only check of an int32 [batch, pt_stride] table and [batch] lengths."""
+    t, tp = _i32_array(table)
+    c, cp = _i32_array(ctx_lens)
+    if t.ndim != 2 or c.shape != (t.shape[0],):
+        raise ValueError("table must be [batch, pt_stride] and ctx_lens [batch]")
+    _check(lib().pkv_page_table_validate(pool.handle, tp, cp, t.shape[0], t.shape[1]))
+
+
+def page_table_write(pool, table, ctx_lens, dev_table, dev_ctx_lens, stream=None):
+    """Validate host arrays, then copy them into int32 device tensors."""
+    import torch
+    t, tp = _i32_array(table)
+    c, cp = _i32_array(ctx_lens)
+    if t.ndim != 2 or c.shape != (t.shape[0],):
+        raise ValueError("table must be [batch, pt_stride] and ctx_lens [batch]")
+    if dev_table.numel() < t.size or dev_ctx_lens.numel() < c.size:
+        raise ValueError("device table / ctx_lens tensors are too small")
+    _check(lib().pkv_page_table_write(pool.handle, tp, cp, t.shape[0], t.shape[1],
+                                      _ptr(dev_table, torch.int32, "dev_table"),
+                                      _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"),
+                                      _stream(stream)))
+
+
+def decode_workspace_bytes(batch, num_q_heads, token_count, tile_tokens, head_dim=256,
+                           kernel=0, split_tokens=0):
+    out = U64()
+    o = _opts(kernel, split_tokens)
+    _check(lib().pkv_decode_workspace_bytes(batch, num_q_heads, head_dim, token_count,
+                                            tile_tokens, ctypes.byref(o), ctypes.byref(out)))
+    return out.value
+
+
+def decode_attention(pool, layer, q, dev_table, dev_ctx_lens, token_begin, token_count,
+                     tile_tokens, scale, part_out, part_lse, workspace=None, kernel=0,
+                     split_tokens=0, stream=None):
+    """Tile partials of one layer for tokens [token_begin, token_begin + token_count).
+
+    q: bf16 [B, Hq, D]; dev_table: int32 [B, pt_stride] (entry i = logical page
+    token_begin/64 + i); part_out: fp32 [B, Hq, num_slots, D]; part_lse: fp32
+    [B, Hq, num_slots]."""
+    import torch
+    B, Hq, D = q.shape
+    if part_out.dim() != 4 or part_out.shape[:2] != (B, Hq) or part_out.shape[3] != D:
+        raise ValueError("part_out must be [B, Hq, num_slots, D]")
+    num_slots = part_out.shape[2]
+    if tuple(part_lse.shape) != (B, Hq, num_slots):
+        raise ValueError("part_lse must be [B, Hq, num_slots]")
+    if dev_table.dim() != 2 or dev_table.shape[0] != B:
+        raise ValueError("dev_table must be [B, pt_stride]")
+    if dev_table.stride(1) != 1:
+        raise ValueError("dev_table rows must be contiguous")
+    o = _opts(kernel, split_tokens)
+    ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pkv_decode_attention(
+        pool.handle, int(layer), _ptr(q, torch.bfloat16, "q"),
+        dev_table.data_ptr(), int(dev_table.stride(0)),
+        _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"), B, Hq,
+        int(token_begin), int(token_count), int(tile_tokens), float(scale),
+        _ptr(part_out, torch.float32, "part_out"), _ptr(part_lse, torch.float32, "part_lse"),
+        num_slots, ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def merge_partials(part_out, part_lse, out, lse, stream=None):
+    """FP32 LSE merge of every slot of each row: part_out [..., S, D] -> out [..., D]."""
+    import torch
+    D = part_out.shape[-1]
+    S = part_out.shape[-2]
+    rows = part_out.numel() // (S * D)
+    if part_lse.numel() != rows * S or out.numel() != rows * D or lse.numel() != rows:
+        raise ValueError("part_lse / out / lse shapes do not match part_out")
+    _check(lib().pkv_merge_partials(
+        _ptr(part_out, torch.float32, "part_out"), _ptr(part_lse, torch.float32, "part_lse"),
+        rows, S, D, _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _stream(stream)))

@@ -1,0 +1,150 @@
+"""Helpers for the GPU tests: build a device arena from the seeded generator,
+run the library through its binding, and compare with the float64 oracle."""
+
+import math
+
+import numpy as np
+import torch
+
+from paged_kv_cache_10_amd import inputs as I
+from paged_kv_cache_10_amd import pkv
+import oracle
+
+OUT_TOL = 2e-3     # max abs error on outputs
+LSE_TOL = 1e-4     # abs error on log-sum-exp
+
+DEV = "cuda:0"
+
+
+class Case:
+    """A workload resident on the device: arena, pool, tables, queries."""
+
+    def __init__(self, w, layers=None, fill=0, host=True, table=None):
+        self.w = w
+        self.layers = list(range(w.num_layers)) if layers is None else list(layers)
+        # rows cover whole 32,768-token staging windows, so every tile length
+        # used here (all divide 32,768) has its window inside the row
+        width = max(1, -(-w.max_ctx // 32768)) * (32768 // w.page_tokens)
+        self.table = I.draw_page_tables(w, width) if table is None else np.asarray(table, np.int32)
+        self.ctx = np.array(w.ctx_lens, dtype=np.int32)
+        pb = w.page_layer_bytes * w.num_layers
+        self.arena = torch.empty(w.num_pages * pb // 2, dtype=torch.int16, device=DEV)
+        self.arena.fill_(int(np.uint16(fill).view(np.int16)))
+        self.pool = pkv.Pool(self.arena, w.num_layers, w.num_kv_heads, w.head_dim, w.page_tokens)
+        self.dev_table = torch.empty(self.table.shape, dtype=torch.int32, device=DEV)
+        self.dev_ctx = torch.empty(w.batch, dtype=torch.int32, device=DEV)
+        pkv.page_table_write(self.pool, self.table, self.ctx, self.dev_table, self.dev_ctx)
+        self.host = host
+        self.q = {}
+        for layer in self.layers:
+            if host:
+                qb = I.draw_q(w, layer)
+                self.q[layer] = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(DEV)
+            else:
+                self.q[layer] = I.device_q(w, layer, DEV)
+            for b in range(w.batch):
+                k, v = self.logical_kv_dev(layer, b)
+                I.device_scatter(self.arena, w, layer, b, self.table[b], k, v, pad_value=fill)
+        torch.cuda.synchronize()
+
+    def logical_kv_dev(self, layer, b):
+        if self.host:
+            kb, vb = I.draw_kv(self.w, layer, b)
+            k = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
+            v = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
+            return k, v
+        return I.device_kv(self.w, layer, b, DEV)
+
+    def logical_kv_f64(self, layer, b):
+        """Oracle inputs: the generator's bf16 bits widened to float64."""
+        if self.host:
+            kb, vb = I.draw_kv(self.w, layer, b)
+        else:
+            k, v = I.device_kv(self.w, layer, b, DEV)
+            kb = k.view(torch.int16).cpu().numpy().view(np.uint16)
+            vb = v.view(torch.int16).cpu().numpy().view(np.uint16)
+        return oracle.widen_bf16(kb), oracle.widen_bf16(vb)
+
+    def q_f64(self, layer):
+        return oracle.widen_bf16(self.q[layer].view(torch.int16).cpu().numpy().view(np.uint16))
+
+    def num_slots(self, tile):
+        return max(1, -(-self.w.max_ctx // tile))
+
+    def decode(self, layer, tile=None, kernel=0, split=0, staged=None, out=None):
+        """Tile partials for every request of one layer, then the merge.
+        staged: window length for staged calls (None = one resident call).
+        Returns torch tensors (part_o, part_lse, out, lse)."""
+        w = self.w
+        tile = tile or w.tile_tokens
+        S = self.num_slots(tile)
+        span = S * tile
+        B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+        if out is None:
+            po = torch.full((B, Hq, S, D), float("nan"), device=DEV)
+            pl = torch.full((B, Hq, S), float("nan"), device=DEV)
+            o = torch.empty((B, Hq, D), device=DEV)
+            l = torch.empty((B, Hq), device=DEV)
+        else:
+            po, pl, o, l = out
+        window = span if staged is None else staged
+        ws_bytes = pkv.decode_workspace_bytes(B, Hq, window, tile, D, kernel, split)
+        ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+        for begin in range(0, span, window):
+            count = min(window, span - begin)
+            tab = self.dev_table[:, begin // w.page_tokens:]
+            pkv.decode_attention(self.pool, layer, self.q[layer], tab, self.dev_ctx, begin, count,
+                                 tile, w.scale, po, pl, workspace=ws, kernel=kernel,
+                                 split_tokens=split)
+        pkv.merge_partials(po, pl, o, l)
+        torch.cuda.synchronize()
+        return po, pl, o, l
+
+    def oracle_layer(self, layer, tile=None, requests=None):
+        """float64 (tile partials, one-pass out, lse) per request."""
+        w = self.w
+        tile = tile or w.tile_tokens
+        S = self.num_slots(tile)
+        qf = self.q_f64(layer)
+        res = {}
+        for b in (range(w.batch) if requests is None else requests):
+            k, v = self.logical_kv_f64(layer, b)
+            ctx = w.ctx_lens[b]
+            o_t, l_t = oracle.tile_partials(qf[b], k, v, w.scale,
+                                            oracle.tile_bounds(ctx, tile, S), w.num_kv_heads)
+            out, lse = oracle.decode_one_pass(qf[b], k, v, ctx, w.scale, w.num_kv_heads)
+            res[b] = (o_t, l_t, out, lse)
+        return res
+
+
+def assert_lse_close(got, exp, tol=LSE_TOL, what="lse"):
+    got = np.asarray(got, dtype=np.float64)
+    exp = np.asarray(exp, dtype=np.float64)
+    inf_e = np.isneginf(exp)
+    assert np.array_equal(np.isneginf(got), inf_e), f"{what}: -inf pattern differs"
+    if (~inf_e).any():
+        err = np.abs(got[~inf_e] - exp[~inf_e]).max()
+        assert err <= tol, f"{what}: max abs err {err:.3e} > {tol}"
+
+
+def assert_out_close(got, exp, tol=OUT_TOL, what="out"):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - exp).max() if got.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol}"
+    return err
+
+
+def check_layer(case, layer, got, ref, tile=None):
+    po, pl, o, l = [t.cpu().numpy() for t in got]
+    worst = 0.0
+    for b, (o_t, l_t, out, lse) in ref.items():
+        worst = max(worst, assert_out_close(po[b], o_t, what=f"partials b={b}"))
+        assert_lse_close(pl[b], l_t, what=f"partial lse b={b}")
+        worst = max(worst, assert_out_close(o[b], out, what=f"out b={b}"))
+        assert_lse_close(l[b], lse, what=f"lse b={b}")
+    return worst
+
+
+def same_bits(a, b):
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))

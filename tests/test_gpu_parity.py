@@ -1,0 +1,153 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle,
+element by element, plus the bitwise properties the pages ask of it.
+
+Tolerances: max abs error 2e-3 on outputs and 1e-4 on log-sum-exp."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_10_amd import inputs as I
+import oracle
+from gpu_helpers import (Case, DEV, assert_lse_close, assert_out_close, check_layer, same_bits)
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = ["valu", "mfma"]
+
+
+def ragged_workload(**over):
+    # lengths around page and tile edges, one empty request
+    w = I.Workload("ragged", seed=11, ctx_lens=[1, 63, 64, 65, 1000, 2049, 0, 4097],
+                   num_layers=2, tile_tokens=1024)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+@pytest.fixture(scope="module")
+def tiny(gpu):
+    return Case(I.workload("tiny"))
+
+
+@pytest.fixture(scope="module")
+def ragged(gpu):
+    return Case(ragged_workload(), fill=I.BF16_QNAN)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_tiny_partials_and_merge(tiny, kernel):
+    """1 request x 4,096 tokens, tile 1,024: four partials and their merge."""
+    got = tiny.decode(0, kernel=kernel)
+    ref = tiny.oracle_layer(0)
+    err = check_layer(tiny, 0, got, ref)
+    print(f"tiny {kernel}: max abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("tile,split", [(1024, 0), (256, 0), (2048, 64), (64, 0), (4096, 1024)])
+def test_ragged_lengths(ragged, kernel, tile, split):
+    """Lengths 0, 1, 63, 64, 65, 1000, 2049, 4097 on a NaN-poisoned arena,
+    for tiles that are and are not one work-group's split."""
+    for layer in (0, 1):
+        got = ragged.decode(layer, tile=tile, kernel=kernel, split=split)
+        ref = ragged.oracle_layer(layer, tile=tile)
+        check_layer(ragged, layer, got, ref)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_run_to_run_and_staged_bitwise(ragged, kernel):
+    """Reflexive control (two identical runs agree bit for bit), then staged
+    windows of 2,048 tokens against one resident call at the same tiling."""
+    a = ragged.decode(1, tile=512, kernel=kernel)
+    b = ragged.decode(1, tile=512, kernel=kernel)
+    for x, y in zip(a, b):
+        assert same_bits(x, y)
+    c = ragged.decode(1, tile=512, kernel=kernel, staged=2048)
+    for x, y in zip(a, c):
+        assert same_bits(x, y)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_poisoned_padding_and_placement(gpu, kernel):
+    """Padding (NaN vs 0) and the physical placement of pages change no bit."""
+    w = ragged_workload(num_layers=1)
+    base = Case(w, fill=0)
+    ref = base.decode(0, kernel=kernel)
+    pois = Case(w, fill=I.BF16_QNAN)
+    for x, y in zip(ref, pois.decode(0, kernel=kernel)):
+        assert same_bits(x, y)
+    perm = np.random.default_rng(99).permutation(w.num_pages).astype(np.int32)
+    t2 = np.where(base.table >= 0, perm[np.maximum(base.table, 0)], -1).astype(np.int32)
+    moved = Case(w, fill=I.BF16_QNAN, table=t2)
+    for x, y in zip(ref, moved.decode(0, kernel=kernel)):
+        assert same_bits(x, y)
+
+
+def test_kernels_agree(ragged):
+    """VALU and MFMA kernels agree with each other within the tolerance."""
+    a = ragged.decode(0, tile=1024, kernel="valu")
+    b = ragged.decode(0, tile=1024, kernel="mfma")
+    assert torch.isneginf(a[3]).equal(torch.isneginf(b[3]))
+    assert (a[2] - b[2]).abs().max().item() <= 2e-3
+
+
+# ---------------------------------------------------------------- merge --
+
+
+@pytest.fixture(scope="module")
+def stress(gpu):
+    """64 x 24 x 256 partials of width 256, lse ~ U[-40, 40], ~10 % empty,
+    built by the oracle from explicit keys (4 per partial)."""
+    d = I.stress_draws()
+    o, lse, scores = oracle.stress_partials(d["r"], d["vals"], d["target_lse"], d["empty"])
+    uo, ul = oracle.union_attention(scores, d["vals"])
+    po = torch.from_numpy(o.astype(np.float32)).to(DEV)
+    pl = torch.from_numpy(lse.astype(np.float32)).to(DEV)
+    return po, pl, uo, ul
+
+
+def merge(po, pl):
+    from paged_kv_cache_10_amd import pkv
+    rows = po.shape[:-2]
+    out = torch.empty(rows + (po.shape[-1],), device=DEV)
+    lse = torch.empty(rows, device=DEV)
+    pkv.merge_partials(po, pl, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_merge_stress_matches_union_softmax(stress):
+    po, pl, uo, ul = stress
+    out, lse = merge(po, pl)
+    assert_out_close(out.cpu().numpy(), uo)
+    assert_lse_close(lse.cpu().numpy(), ul)
+    # the forced rows: (0,0) all empty, (0,1) one live partial
+    assert torch.all(out[0, 0] == 0) and lse[0, 0].item() == -math.inf
+    live = int(np.flatnonzero(np.isfinite(pl[0, 1].cpu().numpy()))[0])
+    assert same_bits(out[0, 1], po[0, 1, live]) and same_bits(lse[0, 1], pl[0, 1, live])
+
+
+def test_merge_identity_and_empty_insertion_bitwise(stress):
+    po, pl, _, _ = stress
+    # one slot merges to itself, bit for bit
+    o1, l1 = merge(po[:, :, 7:8].contiguous(), pl[:, :, 7:8].contiguous())
+    live = torch.isfinite(pl[:, :, 7])
+    assert same_bits(o1[live], po[:, :, 7][live]) and same_bits(l1[live], pl[:, :, 7][live])
+    # inserting empty slots (lse = -inf, output NaN) changes no bit
+    ref = merge(po, pl)
+    S = po.shape[2]
+    ins = [0, 5, 5, 100, S]
+    parts_o, parts_l = [], []
+    prev = 0
+    for i in ins:
+        parts_o.append(po[:, :, prev:i])
+        parts_l.append(pl[:, :, prev:i])
+        parts_o.append(torch.full_like(po[:, :, :1], float("nan")))
+        parts_l.append(torch.full_like(pl[:, :, :1], -math.inf))
+        prev = i
+    got = merge(torch.cat(parts_o, 2).contiguous(), torch.cat(parts_l, 2).contiguous())
+    for x, y in zip(ref, got):
+        assert same_bits(x, y)
