@@ -1,0 +1,254 @@
+"""Decode-attention benchmark on one MI355X.
+
+One step = one decode token for every request: for each of the 16 layers,
+pkv_decode_attention (split-KV tile partials) then pkv_merge_partials (FP32
+LSE merge).  Default workload: 1 request x 262,144 tokens, 16 layers, 24 q /
+4 KV heads, head_dim 256, bf16, 64-token pages in a 16 GiB arena in random
+physical order, 1 % of keys scaled by 4; the history is cut into eight
+32,768-token tiles, each split-KV inside, and all partials are merged in
+FP32.  Inputs are synthetic (seeded) and resident in HBM before timing.
+
+Prints one JSON line.  `value` is KV GB/s: K+V bytes the exact path must read
+per step (sum of lengths x 4,096 B x 16 layers) over the step time.
+
+    python bench.py [--steps K] [--warmup W] [--workload long262k|conc|mixed]
+                    [--tile T] [--split S] [--kernel mfma|valu] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long262k")
+    ap.add_argument("--tile", type=int, default=0, help="tile tokens (default: workload's)")
+    ap.add_argument("--split", type=int, default=0, help="tokens per work-group (0: library default)")
+    ap.add_argument("--kernel", default="mfma", choices=["mfma", "valu"])
+    ap.add_argument("--staged", action="store_true",
+                    help="decode each 32,768-token staging window with its own call")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 1 GiB device copy (the PMC calibration kernel)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path exists)", file=sys.stderr)
+        return 2
+    import torch
+    from paged_kv_cache_10_amd import inputs as I
+    from paged_kv_cache_10_amd import pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pkv.lib()
+
+    w = I.workload(args.workload)
+    if args.workload == "long262k":
+        w.tile_tokens = 32768            # eight staging tiles, each split-KV inside
+    if args.tile:
+        w.tile_tokens = args.tile
+    T = w.tile_tokens
+    B, Hq, Hkv, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
+
+    # ---------------------------------------------------------------- inputs
+    t_gen = time.time()
+    slots = -(-w.max_ctx // T)
+    span = slots * T
+    width = span // w.page_tokens
+    table = I.draw_page_tables(w, width)
+    ctx = np.array(w.ctx_lens, dtype=np.int32)
+    arena = torch.empty(w.num_pages * w.page_layer_bytes * L // 2, dtype=torch.int16, device=dev)
+    arena.zero_()
+    pool = pkv.Pool(arena, L, Hkv, D, w.page_tokens)
+    dt = torch.empty(table.shape, dtype=torch.int32, device=dev)
+    dc = torch.empty(B, dtype=torch.int32, device=dev)
+    pkv.page_table_write(pool, table, ctx, dt, dc)
+    qs = []
+    for layer in range(L):
+        qs.append(I.device_q(w, layer, dev))
+        for b in range(B):
+            k, v = I.device_kv(w, layer, b, dev)
+            I.device_scatter(arena, w, layer, b, table[b], k, v)
+            del k, v
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    po = torch.empty((B, Hq, slots, D), device=dev)
+    pl = torch.empty((B, Hq, slots), device=dev)
+    outs = torch.empty((L, B, Hq, D), device=dev)
+    lses = torch.empty((L, B, Hq), device=dev)
+    window = 32768 if args.staged else span
+    ws_bytes = pkv.decode_workspace_bytes(B, Hq, window, T, D, args.kernel, args.split)
+    ws = torch.empty(max(16, ws_bytes) // 4 + 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def decode_layer(layer, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for begin in range(0, span, window):
+            pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc, begin,
+                                 min(window, span - begin), T, w.scale, po, pl, workspace=ws,
+                                 kernel=args.kernel, split_tokens=args.split, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.merge_partials(po, pl, outs[layer], lses[layer], stream=stream)
+
+    def step(evs=None):
+        for layer in range(L):
+            decode_layer(layer, None if evs is None else evs[layer])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed
+    K = args.steps
+    ev_dec = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)] for _ in range(K)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(K):
+        step(ev_dec[k])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / K
+    dec_ms = [a.elapsed_time(b) for evk in ev_dec for (a, b) in evk]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    kv_bytes_step = w.kv_bytes_per_step
+    kv_gbs = kv_bytes_step / (ms_step * 1e-3) / 1e9
+    tok_s = B / (ms_step * 1e-3)
+    kv_bytes_layer = kv_bytes_step // L
+    dec_gbs = kv_bytes_layer / (dec_avg_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "decode attention KV GB/s (% of HBM peak) and tokens/s at 262K ctx, 1 GPU",
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {B} x {w.max_ctx if B == 1 else 'mixed'} tokens, {L} layers, "
+                        f"{Hq} q / {Hkv} kv heads, head_dim {D}, 64-token pages, tile {T}"
+                        + (", staged 32768-token windows" if args.staged else ""),
+            "batch": B, "ctx_lens_sum": int(sum(w.ctx_lens)), "layers": L, "tile_tokens": T,
+            "kernel": args.kernel, "split_tokens": args.split or "default",
+            "parallelism": "none (1 GPU)",
+        },
+        "tokens_per_s": round(tok_s, 2),
+        "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": kv_bytes_step,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pkv_decode_attention (split-KV decode"
+                      + ("" if ws_bytes == 0 else " + tile finalize") + "), one layer per launch",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": kv_bytes_layer,
+            "avg_launch_ms": round(dec_avg_ms, 5),
+            "traffic": None,
+        },
+        "setup_s": round(t_gen, 1),
+    }
+
+    if args.copy_probe:
+        n = 1 << 29
+        src = torch.empty(n, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / 10
+        res["copy_probe"] = {"bytes_read": n * 2, "bytes_written": n * 2, "ms": round(cms, 4),
+                             "GBs_read_plus_write": round(4 * n / (cms * 1e-3) / 1e9, 1)}
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, qs, args.cpu_seconds)
+
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(w, qs, budget_s):
+    """The float64 oracle on this host's cores, on a bounded sample: whole
+    layers of the same workload (all requests, all heads, one-pass exact
+    attention), as many as fit the budget; scaled to tokens/s per step."""
+    import torch
+    import oracle
+    from paged_kv_cache_10_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    spent = 0.0
+    layers = 0
+    for layer in range(w.num_layers):
+        qb = qs[layer].view(torch.int16).cpu().numpy().view(np.uint16)
+        kv = []
+        for b in range(w.batch):
+            k, v = I.device_kv(w, layer, b, "cuda:0")
+            kv.append((k.view(torch.int16).cpu().numpy().view(np.uint16),
+                       v.view(torch.int16).cpu().numpy().view(np.uint16)))
+            del k, v
+        t = time.time()
+        for b in range(w.batch):
+            oracle.decode_one_pass(oracle.widen_bf16(qb[b]), oracle.widen_bf16(kv[b][0]),
+                                   oracle.widen_bf16(kv[b][1]), w.ctx_lens[b], w.scale,
+                                   w.num_kv_heads)
+        spent += time.time() - t
+        layers += 1
+        del kv
+        if spent >= budget_s:
+            break
+    s_per_step = spent / layers * w.num_layers
+    return {
+        "value": round(w.batch / s_per_step, 4),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{layers} of {w.num_layers} layers of the same workload (all "
+                  f"{w.batch} request(s), all heads, float64 one-pass), scaled x{w.num_layers / layers:.1f}",
+        "seconds": round(spent, 2),
+        "kv_GBs_equiv": round(w.kv_bytes_per_step / s_per_step / 1e9, 3),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())
