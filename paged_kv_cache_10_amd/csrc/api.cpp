@@ -41,7 +41,7 @@ int ok() {
   return PKV_OK;
 }
 
-constexpr int kDefaultSplit = 512;   // tokens per work-group unless the caller says otherwise
+constexpr int kDefaultSplit = 2048;  // tokens per work-group unless the caller says otherwise
 
 int check_geom(const pkv_geom* g) {
   if (!g) return fail(PKV_ERR_INVALID_ARG, "geom is NULL");
@@ -310,8 +310,8 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   pkv::DecodeArgs a;
   a.arena = static_cast<const uint16_t*>(pool->base);
-  a.page_elems = (int64_t)(pool->page_bytes / 2);
-  a.layer_off = (int64_t)(pool->page_layer_bytes / 2) * layer;
+  a.page_elems = (int64_t)(pool->page_layer_bytes / 2);
+  a.layer_off = (int64_t)(pool->page_layer_bytes / 2) * pool->num_pages * layer;
   a.num_pages = (int32_t)pool->num_pages;
   a.num_kv_heads = G.num_kv_heads;
   a.q = static_cast<const uint16_t*>(q);

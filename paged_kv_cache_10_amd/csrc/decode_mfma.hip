@@ -24,6 +24,8 @@
 // Padding (tokens at or past the length, or pages whose id is out of range)
 // scores -inf and its V values are zeroed before the MFMA, so NaN padding
 // never reaches the sums.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -58,15 +60,110 @@ __device__ __forceinline__ uint4 mask_pairs(uint4 u, int live) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-struct Chunk {
-  const uint16_t* k;     // K block of the page (token-major)
-  const uint16_t* v;     // V block of the page (dim-major)
-  int base;              // first token of the chunk within the page (0 or 32)
-  int live;              // tokens of the chunk that exist (0..32)
+// Addresses of one page of one KV head for one wave.
+struct PageRef {
+  const uint16_t* k;     // K block (token-major [64][256])
+  const uint16_t* v;     // V block (dim-major [256][64])
+  int valid;             // tokens of the page that exist (0..64)
 };
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
+// K operand of a 32-token chunk (half `base`/32 of the page): 16 loads of
+// 1 KiB, tile t and k-step kb at piece (t*8 + kb)*64 + lane.
+__device__ __forceinline__ void load_k(uint4 (&kr)[2][8], const PageRef& pg, int base, int lane) {
+  const uint4* p = reinterpret_cast<const uint4*>(pg.k) + (base >> 5) * 1024 + lane;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) kr[t][kb] = p[(t * 8 + kb) * 64];
+}
+
+// V^T operand of a 32-token chunk: channel block db at piece db*64 + lane.
+__device__ __forceinline__ void load_v(uint4 (&vr)[16], const PageRef& pg, int base, int lane) {
+  const uint4* p = reinterpret_cast<const uint4*>(pg.v) + (base >> 5) * 1024 + lane;
+#pragma unroll
+  for (int db = 0; db < 16; ++db) vr[db] = p[db * 64];
+}
+
+// One 32-token chunk: QK, online softmax, PV.  `live` = tokens of the chunk
+// that exist.  With kNext, the next chunk's K loads are issued as soon as QK
+// has consumed kr, and its V loads as soon as PV has consumed vr.
+template <bool kNext>
+__device__ __forceinline__ void chunk(uint4 (&kr)[2][8], uint4 (&vr)[16], f32x4_t (&acc)[16],
+                                      float& m, float& lsum, const uint16_t* qrow, int live,
+                                      float scale_log2, int q, int lane,
+                                      const PageRef& nxt, int nbase) {
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  asm volatile("" ::: "memory");     // keep the LDS operand reads inside the loop
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const bf16x8_t qb = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * kb));
+    s0 = mfma(as_bf16x8(kr[0][kb]), qb, s0);
+    s1 = mfma(as_bf16x8(kr[1][kb]), qb, s1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kNext) load_k(kr, nxt, nbase, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // online softmax; lane holds tokens 8q + e, e = 0..7, of head n (base 2)
+  float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s[e] = (8 * q + e < live) ? s[e] * scale_log2 : -INFINITY;
+    cmax = fmaxf(cmax, s[e]);
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  const float mn = fmaxf(m, cmax);
+  const float mref = (mn == -INFINITY) ? 0.f : mn;
+  const float alpha = fast_exp2(m - mref);
+  m = mn;
+  float p[8];
+  float ps = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = fast_exp2(s[e] - mref);
+    ps += p[e];
+  }
+  lsum = lsum * alpha + ps;
+  if (__any(alpha != 1.f)) {           // multiplying by 1 is exact: skipping changes no bit
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      acc[db][0] *= alpha;
+      acc[db][1] *= alpha;
+      acc[db][2] *= alpha;
+      acc[db][3] *= alpha;
+    }
+  }
+  bf16x8_t phi, plo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)p[e];
+    phi[e] = h;
+    plo[e] = (__bf16)(p[e] - (float)h);
+  }
+  if (live < 32) {
+    const int vlive = max(0, min(8, live - 8 * q));
+#pragma unroll
+    for (int db = 0; db < 16; ++db) vr[db] = mask_pairs(vr[db], vlive);
+  }
+  // PV: all hi products, then all lo products (independent MFMAs back to back)
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = mfma(as_bf16x8(vr[db]), phi, acc[db]);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = mfma(as_bf16x8(vr[db]), plo, acc[db]);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kNext) load_v(vr, nxt, nbase, lane);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+#ifndef PKV_MFMA_RING
+#define PKV_MFMA_RING 1
+#endif
+
+template <int G, int kRing>
+__global__ __launch_bounds__(kThreads)
+void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
@@ -101,14 +198,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  bf16x8_t qb[8];   // B operand of QK: head n, channels 32kb + 8q .. +7
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-    qb[kb] = as_bf16x8(*reinterpret_cast<const uint4*>(&q_lds[n * kQPad + 32 * kb + 8 * q]));
-
-  // rows of the two QK tiles: tile row r of tile t holds token 8(r/4) + 4t + r%4
-  const int krow0 = 8 * (n >> 2) + (n & 3);
-  const int krow1 = krow0 + 4;
+  // B operand of QK (head n, channels 32kb + 8q .. +7) is read from LDS at
+  // every use rather than held in 32 registers.
+  const uint16_t* qrow = &q_lds[n * kQPad + 8 * q];
 
   float m = -INFINITY;   // running max of head n (base 2), same in the 4 lanes of a head
   float lsum = 0.f;      // this lane's share of the running sum
@@ -120,113 +212,67 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
   const int32_t* trow = a.table + (int64_t)b * a.pt_stride;
   const int first_page = (t0 - a.token_begin) / PT;
   const int n_pages = (t1 > t0) ? (t1 - t0 + PT - 1) / PT : 0;
-  // this wave's pages: w, w + 4, ... ; two chunks each
+  // this wave's pages: w, w + 4, ...
   const int my_pages = (n_pages > w) ? (n_pages - w + kWaves - 1) / kWaves : 0;
-  const int n_chunks = 2 * my_pages;
 
-  auto chunk_at = [&](int ci) {
-    const int pi = w + kWaves * (ci >> 1);
-    const int tok = t0 + pi * PT;
-    int phys = trow[first_page + pi];
-    int valid = min(PT, t1 - tok);
-    if (phys < 0 || phys >= a.num_pages) { phys = 0; valid = 0; }   // read page 0, mask all
+  // Page ids of this wave's pages (at most 64: split_tokens <= 16384): lane j
+  // holds the id of the wave's page j, fetched once before the loop and read
+  // with readlane, so no dependent global load sits in front of K/V loads.
+  const int my_id = (lane < my_pages) ? trow[first_page + w + kWaves * lane] : 0;
+  auto page_at = [&](int j) {
+    PageRef pg;
+    int phys = __builtin_amdgcn_readlane(my_id, j);
+    pg.valid = min(PT, t1 - (t0 + (w + kWaves * j) * PT));
+    if (phys < 0 || phys >= a.num_pages) { phys = 0; pg.valid = 0; }   // read page 0, mask all
     const uint16_t* page = layer_base + (int64_t)phys * a.page_elems;
-    Chunk c;
-    c.k = page + (int64_t)g * PT * D;
-    c.v = page + (int64_t)(a.num_kv_heads + g) * PT * D;
-    c.base = 32 * (ci & 1);
-    c.live = max(0, min(32, valid - c.base));
-    return c;
+    pg.k = page + (int64_t)g * PT * D;
+    pg.v = page + (int64_t)(a.num_kv_heads + g) * PT * D;
+    return pg;
   };
 
-  uint4 kreg[2][8];     // [tile][kb]
-  uint4 vreg[16];       // [db]
-  auto load_k = [&](const Chunk& c) {
-    const uint16_t* r0 = c.k + (c.base + krow0) * D + 8 * q;
-    const uint16_t* r1 = c.k + (c.base + krow1) * D + 8 * q;
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      kreg[0][kb] = *reinterpret_cast<const uint4*>(r0 + 32 * kb);
-      kreg[1][kb] = *reinterpret_cast<const uint4*>(r1 + 32 * kb);
+  // Two register buffers (A: tokens 0-31, B: tokens 32-63 of a page).  While
+  // a chunk computes, the other chunk's loads and the next page's loads of
+  // the buffer just consumed are in flight.
+  uint4 kA[2][8], kB[2][8], vA[16], vB[16];
+  if constexpr (kRing == 2) {
+    if (my_pages > 0) {
+      PageRef cur = page_at(0);
+      load_k(kA, cur, 0, lane);
+      load_v(vA, cur, 0, lane);
+      load_k(kB, cur, 32, lane);
+      load_v(vB, cur, 32, lane);
+      for (int j = 0; j + 1 < my_pages; ++j) {
+        const PageRef nxt = page_at(j + 1);
+        chunk<true>(kA, vA, acc, m, lsum, qrow, min(32, cur.valid), a.scale_log2, q, lane,
+                    nxt, 0);
+        chunk<true>(kB, vB, acc, m, lsum, qrow, max(0, cur.valid - 32), a.scale_log2, q, lane,
+                    nxt, 32);
+        cur = nxt;
+      }
+      chunk<false>(kA, vA, acc, m, lsum, qrow, min(32, cur.valid), a.scale_log2, q, lane, cur,
+                   0);
+      chunk<false>(kB, vB, acc, m, lsum, qrow, max(0, cur.valid - 32), a.scale_log2, q, lane,
+                   cur, 32);
     }
-  };
-  auto load_v = [&](const Chunk& c) {
-    const uint16_t* p = c.v + n * PT + c.base + 8 * q;
-#pragma unroll
-    for (int db = 0; db < 16; ++db) vreg[db] = *reinterpret_cast<const uint4*>(p + 16 * db * PT);
-  };
-
-  Chunk cur;
-  if (n_chunks > 0) {
-    cur = chunk_at(0);
-    load_k(cur);
-    load_v(cur);
-  }
-  for (int ci = 0; ci < n_chunks; ++ci) {
-    // ---- QK
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      s0 = mfma(as_bf16x8(kreg[0][kb]), qb[kb], s0);
-      s1 = mfma(as_bf16x8(kreg[1][kb]), qb[kb], s1);
-    }
-    Chunk nxt;
-    const bool more = ci + 1 < n_chunks;
-    if (more) {
-      nxt = chunk_at(ci + 1);
-      load_k(nxt);
-    }
-
-    // ---- online softmax; lane holds tokens 8q + e, e = 0..7, of head n
-    float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s[e] = (8 * q + e < cur.live) ? s[e] * a.scale_log2 : -INFINITY;
-      cmax = fmaxf(cmax, s[e]);
-    }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float mn = fmaxf(m, cmax);
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    m = mn;
-    float p[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(s[e] - mref);
-      ps += p[e];
-    }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      acc[db][0] *= alpha;
-      acc[db][1] *= alpha;
-      acc[db][2] *= alpha;
-      acc[db][3] *= alpha;
-    }
-    bf16x8_t phi, plo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 h = (__bf16)p[e];
-      phi[e] = h;
-      plo[e] = (__bf16)(p[e] - (float)h);
-    }
-
-    // ---- PV
-    const int vlive = max(0, min(8, cur.live - 8 * q));
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      uint4 vv = vreg[db];
-      if (cur.live < 32) vv = mask_pairs(vv, vlive);
-      const bf16x8_t va = as_bf16x8(vv);
-      acc[db] = mfma(va, phi, acc[db]);
-      acc[db] = mfma(va, plo, acc[db]);
-    }
-    if (more) {
-      load_v(nxt);
-      cur = nxt;
+  } else {
+    // one buffer: the next chunk's K (V) loads follow QK (PV) of this chunk
+    const int n_chunks = 2 * my_pages;
+    if (n_chunks > 0) {
+      PageRef cur = page_at(0);
+      int cbase = 0;
+      load_k(kA, cur, 0, lane);
+      load_v(vA, cur, 0, lane);
+      for (int ci = 0; ci + 1 < n_chunks; ++ci) {
+        const int ni = ci + 1;
+        const PageRef nxt = (ni & 1) ? cur : page_at(ni >> 1);
+        const int nbase = 32 * (ni & 1);
+        chunk<true>(kA, vA, acc, m, lsum, qrow, max(0, min(32, cur.valid - cbase)), a.scale_log2,
+                    q, lane, nxt, nbase);
+        cur = nxt;
+        cbase = nbase;
+      }
+      chunk<false>(kA, vA, acc, m, lsum, qrow, max(0, min(32, cur.valid - cbase)), a.scale_log2, q,
+                   lane, cur, cbase);
     }
   }
 
@@ -273,7 +319,7 @@ template <int G>
 hipError_t launch_g(const DecodeArgs& a, int batch, hipStream_t stream) {
   const int n_split = a.token_count / a.split_tokens;
   dim3 grid(n_split, a.num_kv_heads, batch);
-  hipLaunchKernelGGL(decode_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, PKV_MFMA_RING>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

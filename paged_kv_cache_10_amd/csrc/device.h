@@ -27,14 +27,33 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // 2^x on the transcendental unit; 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pool block layout.  A (layer, page, K|V, kv head) block holds 64 tokens x
+// 256 channels as 2,048 pieces of 16 bytes (8 bf16), stored in the order the
+// MFMA kernel's wave loads consume them: 64 consecutive pieces (1 KiB) per
+// load instruction, lane l taking piece l, so every load is one contiguous
+// 1 KiB read.
+//   K piece (token j, channels 8c..8c+7): h = j/32 (32-token half), within
+//   the half jj = j%32 goes to MFMA tile t = (jj/4)%2, row r = 4(jj/8)+jj%4,
+//   and the piece to k-step c/4, lane group c%4.
+//   V piece (channel d, tokens 8u..8u+7): half u/4, channel block d/16,
+//   lane group u%4, row d%16.
+__device__ __forceinline__ int k_piece(int j, int c) {
+  const int h = j >> 5, jj = j & 31;
+  const int t = (jj >> 2) & 1, r = 4 * (jj >> 3) + (jj & 3);
+  return ((h * 2 + t) * 8 + (c >> 2)) * 64 + (c & 3) * 16 + r;
+}
+__device__ __forceinline__ int v_piece(int d, int u) {
+  return ((u >> 2) * 16 + (d >> 4)) * 64 + (u & 3) * 16 + (d & 15);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Arguments of one decode launch: per-split partials of one layer.
 struct DecodeArgs {
   const uint16_t* arena;     // bf16 arena
-  int64_t page_elems;        // bf16 elements per physical page (all layers)
-  int64_t layer_off;         // element offset of this layer inside a page
+  int64_t page_elems;        // bf16 elements of one (layer, page): 2 x Hkv blocks
+  int64_t layer_off;         // element offset of this layer's slab in the arena
   int32_t num_pages;
   int32_t num_kv_heads;
   const uint16_t* q;         // [batch][num_q_heads][256]

@@ -30,9 +30,15 @@ Two generators, same distributions:
              bits, which is how the oracle gets its copy.
 
 Pool layout written here (the library header documents the same layout):
-  arena = pages[P], page = layers[L], layer block = [K | V][Hkv] blocks of
-  64 x D bf16; a K block is token-major [64][D], a V block is dim-major
-  [D][64].
+  arena = layers[L] x pages[P] x [K | V] x kv heads[Hkv] x one 32 KiB block
+  (64 tokens x 256 channels, bf16).  A block is 2,048 pieces of 16 bytes
+  (8 bf16) stored in the order the decode kernel's wave loads consume them,
+  64 pieces (1 KiB) per load instruction:
+    K piece (token j, channels 8c..8c+7) sits at
+        ((h*2 + t)*8 + c//4)*64 + (c%4)*16 + r
+      with h = j//32, jj = j%32, t = (jj//4)%2, r = 4*(jj//8) + jj%4;
+    V piece (channel d, tokens 8u..8u+7) sits at
+        ((u//4)*16 + d//16)*64 + (u%4)*16 + d%16.
 """
 
 from dataclasses import dataclass, field
@@ -214,23 +220,52 @@ def draw_page_tables(w, width=None):
     return table
 
 
+def _k_piece_order():
+    """For each storage position of a K block, the logical piece j*32 + c
+    (token j, channels 8c..8c+7) it holds."""
+    order = np.empty(2048, dtype=np.int64)
+    for j in range(64):
+        h, jj = divmod(j, 32)
+        t, r = (jj // 4) % 2, 4 * (jj // 8) + jj % 4
+        for c in range(32):
+            order[((h * 2 + t) * 8 + c // 4) * 64 + (c % 4) * 16 + r] = j * 32 + c
+    return order
+
+
+def _v_piece_order():
+    """For each storage position of a V block, the logical piece d*8 + u
+    (channel d, tokens 8u..8u+7) it holds."""
+    order = np.empty(2048, dtype=np.int64)
+    for d in range(256):
+        for u in range(8):
+            order[((u // 4) * 16 + d // 16) * 64 + (u % 4) * 16 + d % 16] = d * 8 + u
+    return order
+
+
+K_PIECES = _k_piece_order()
+V_PIECES = _v_piece_order()
+
+
 def page_blocks(k_bits, v_bits, page_tokens, pad_value=0):
-    """Logical K/V [Hkv, ctx, D] -> per-page blocks in pool layout:
-    K [npages, Hkv, 64*D] token-major, V [npages, Hkv, D*64] dim-major.
-    Tokens past ctx in the last page get pad_value (a bf16 bit pattern)."""
+    """Logical K/V [Hkv, ctx, 256] -> per-page blocks in pool layout,
+    [npages, Hkv, 64*256] each.  Tokens past ctx in the last page get
+    pad_value (a bf16 bit pattern)."""
     Hkv, ctx, D = k_bits.shape
+    assert D == 256 and page_tokens == 64
     n = -(-ctx // page_tokens)
     kp = np.full((Hkv, n * page_tokens, D), pad_value, dtype=np.uint16)
     vp = np.full((Hkv, n * page_tokens, D), pad_value, dtype=np.uint16)
     kp[:, :ctx] = k_bits
     vp[:, :ctx] = v_bits
-    kb = kp.reshape(Hkv, n, page_tokens * D).transpose(1, 0, 2)
-    vb = vp.reshape(Hkv, n, page_tokens, D).transpose(1, 0, 3, 2).reshape(n, Hkv, D * page_tokens)
+    kl = kp.reshape(Hkv, n, 64 * 32, 8)                               # pieces j*32 + c
+    vl = vp.reshape(Hkv, n, 64, 256).transpose(0, 1, 3, 2).reshape(Hkv, n, 256 * 8, 8)
+    kb = kl[:, :, K_PIECES].reshape(Hkv, n, 64 * D).transpose(1, 0, 2)
+    vb = vl[:, :, V_PIECES].reshape(Hkv, n, 64 * D).transpose(1, 0, 2)
     return np.ascontiguousarray(kb), np.ascontiguousarray(vb)
 
 
 def host_pool(w, table, layers=None, fill=0, pad_value=None):
-    """Build the whole arena on the host as uint16 [P, L, 2, Hkv, 64*D] and
+    """Build the whole arena on the host as uint16 [L, P, 2, Hkv, 64*D] and
     return (pool, kv) with kv[(layer, b)] = (k_bits, v_bits) logical.
 
     layers: which layers to fill (default all); the rest keep `fill`.
@@ -238,7 +273,7 @@ def host_pool(w, table, layers=None, fill=0, pad_value=None):
     if pad_value is None:
         pad_value = fill
     L, Hkv, D, PT = w.num_layers, w.num_kv_heads, w.head_dim, w.page_tokens
-    pool = np.full((w.num_pages, L, 2, Hkv, PT * D), fill, dtype=np.uint16)
+    pool = np.full((L, w.num_pages, 2, Hkv, PT * D), fill, dtype=np.uint16)
     kv = {}
     for layer in (range(L) if layers is None else layers):
         for b in range(w.batch):
@@ -249,8 +284,8 @@ def host_pool(w, table, layers=None, fill=0, pad_value=None):
                 continue
             kb, vb = page_blocks(kbits, vbits, PT, pad_value)
             pages = table[b, :n]
-            pool[pages, layer, 0] = kb
-            pool[pages, layer, 1] = vb
+            pool[layer, pages, 0] = kb
+            pool[layer, pages, 1] = vb
     return pool, kv
 
 
@@ -287,28 +322,33 @@ def device_q(w, layer, device):
 
 
 def device_scatter(pool, w, layer, b, table_row, k, v, pad_value=0):
-    """Write logical K, V (torch bf16 [Hkv, ctx, D]) of one request into the
-    arena `pool` (a contiguous torch int16 tensor of P pages, any shape) at
-    the pages of `table_row`."""
+    """Write logical K, V (torch bf16 [Hkv, ctx, 256]) of one request into the
+    arena `pool` (a contiguous torch int16 tensor of L x P pages, any shape)
+    at the pages of `table_row`, in the pool layout."""
     import torch
     Hkv, ctx, D = k.shape
     PT = w.page_tokens
     n = -(-ctx // PT)
     if n == 0:
         return
-    pages = torch.as_tensor(np.asarray(table_row[:n], dtype=np.int64), device=pool.device)
-    p5 = pool.view(torch.int16).reshape(-1).view(-1, w.num_layers, 2, Hkv, PT * D)
-    def pad(x):
-        if ctx == n * PT:
-            return x
-        y = torch.full((Hkv, n * PT, D), 0, dtype=torch.int16, device=x.device)
-        y.fill_(np.int16(np.uint16(pad_value).view(np.int16)).item())
+    dev = pool.device
+    pages = torch.as_tensor(np.asarray(table_row[:n], dtype=np.int64), device=dev)
+    p5 = pool.view(torch.int16).reshape(-1).view(w.num_layers, -1, 2, Hkv, PT * D)
+    pad16 = int(np.uint16(pad_value).view(np.int16))
+
+    def padded(x):
+        y = torch.full((Hkv, n * PT, D), pad16, dtype=torch.int16, device=dev)
         y[:, :ctx] = x.view(torch.int16)
         return y
-    kk = pad(k.view(torch.int16)).view(Hkv, n, PT * D).permute(1, 0, 2)
-    vv = pad(v.view(torch.int16)).view(Hkv, n, PT, D).permute(1, 0, 3, 2).reshape(n, Hkv, D * PT)
-    p5[pages, layer, 0] = kk.contiguous()
-    p5[pages, layer, 1] = vv.contiguous()
+    kp, vp = padded(k), padded(v)
+    kl = kp.view(Hkv, n, 64 * 32, 8)
+    vl = vp.view(Hkv, n, 64, 256).transpose(2, 3).reshape(Hkv, n, 256 * 8, 8)
+    kidx = torch.as_tensor(K_PIECES, device=dev)
+    vidx = torch.as_tensor(V_PIECES, device=dev)
+    kb = kl[:, :, kidx].reshape(Hkv, n, PT * D).permute(1, 0, 2)
+    vb = vl[:, :, vidx].reshape(Hkv, n, PT * D).permute(1, 0, 2)
+    p5[layer, pages, 0] = kb.contiguous()
+    p5[layer, pages, 1] = vb.contiguous()
 
 
 # ----------------------------------------------------------------------------

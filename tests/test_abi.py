@@ -136,8 +136,9 @@ def ws(batch, hq, count, tile, kernel=0, split=0):
 
 def test_workspace_sizes():
     assert ws(1, 24, 4096, 512) == 0                       # splits are the tiles
-    assert ws(4, 24, 32768, 8192) == 4 * 24 * 64 * 257 * 4   # 512-token splits, 16 per tile
-    assert ws(1, 24, 262144, 32768) == 24 * 512 * 257 * 4
+    assert ws(4, 24, 32768, 8192) == 4 * 24 * 16 * 257 * 4   # 2,048-token splits, 4 per tile
+    assert ws(1, 24, 262144, 32768) == 24 * 128 * 257 * 4
+    assert ws(1, 24, 262144, 32768, split=512) == 24 * 512 * 257 * 4
     assert ws(1, 24, 4096, 1024, split=1024) == 0
     with pytest.raises(pkv.PkvError):
         ws(1, 24, 4096, 1000)
@@ -172,8 +173,8 @@ def decode_raw(pool, **kw):
     (dict(scale=float("inf")), -1, "scale"),
     (dict(q=0), -1, "NULL"),
     (dict(q=(1 << 20) + 2), -1, "aligned"),
-    (dict(ws=0), -4, "workspace"),
-    (dict(ws_bytes=100), -4, "workspace"),
+    (dict(ws=0, tile=4096, slots=1), -4, "workspace"),          # 2,048-token splits
+    (dict(ws_bytes=100, tile=4096, slots=1), -4, "workspace"),
     (dict(split=100), -1, "split_tokens"),
     (dict(batch=-1), -1, "batch"),
 ])

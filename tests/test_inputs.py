@@ -75,33 +75,58 @@ def test_mixed_lengths_in_range():
     assert all(1024 <= c <= 131072 for c in w.ctx_lens)
 
 
+def k_position(j, ch):
+    """Storage position (in 16-byte pieces) of K's token j, channels
+    8*(ch//8)..+7, inside a block, plus the element within the piece: the
+    operand order of the decode kernel (32-token halves, two 16-row tiles,
+    8 k-steps of 32 channels, 4 lane groups of 8 channels, 16 rows)."""
+    half, jj = divmod(j, 32)
+    tile = (jj % 8) // 4
+    row = 4 * (jj // 8) + jj % 4
+    kstep, rem = divmod(ch, 32)
+    group, elem = divmod(rem, 8)
+    return (((half * 2 + tile) * 8 + kstep) * 4 + group) * 16 + row, elem
+
+
+def v_position(j, ch):
+    """Storage position of V's channel ch, token j: pieces hold 8 tokens of
+    one channel; 32-token halves, 16 channel blocks of 16, 4 lane groups."""
+    half, jj = divmod(j, 32)
+    group, elem = divmod(jj, 8)
+    cblock, row = divmod(ch, 16)
+    return ((half * 16 + cblock) * 4 + group) * 16 + row, elem
+
+
 def test_pool_layout():
-    """K block token-major [64][D], V block dim-major [D][64], at the page
-    the table names, in the layer's slot of that page."""
+    """Layer-major arena; block at [layer][page][K|V][kv head]; pieces in
+    the kernel's operand order."""
     w = I.Workload("t", seed=3, ctx_lens=[100, 70], num_layers=2, tile_tokens=64,
-                   num_q_heads=4, num_kv_heads=2, head_dim=8)
+                   num_q_heads=8, num_kv_heads=2, head_dim=256)
     t = I.draw_page_tables(w)
     pool, kv = I.host_pool(w, t, fill=I.BF16_QNAN)
-    assert pool.shape == (w.num_pages, 2, 2, 2, 64 * 8)
+    assert pool.shape == (2, w.num_pages, 2, 2, 64 * 256)
+    g = np.random.default_rng(0)
     for (layer, b), (k, v) in kv.items():
-        for g in range(2):
-            for j in [0, 1, 63, 64, w.ctx_lens[b] - 1]:
+        for kvh in range(2):
+            for j in [0, 1, 5, 31, 32, 63, 64, w.ctx_lens[b] - 1] + g.integers(0, 64, 6).tolist():
                 if j >= w.ctx_lens[b]:
                     continue
                 p = t[b, j // 64]
-                jj = j % 64
-                for d in [0, 3, 7]:
-                    assert pool[p, layer, 0, g, jj * 8 + d] == k[g, j, d]
-                    assert pool[p, layer, 1, g, d * 64 + jj] == v[g, j, d]
+                for ch in [0, 7, 8, 100, 255] + g.integers(0, 256, 6).tolist():
+                    pos, e = k_position(j % 64, ch)
+                    assert pool[layer, p, 0, kvh, pos * 8 + e] == k[kvh, j, ch]
+                    pos, e = v_position(j % 64, ch)
+                    assert pool[layer, p, 1, kvh, pos * 8 + e] == v[kvh, j, ch]
     # padding past ctx in the last page keeps the poison pattern
     p = t[0, 1]
-    assert pool[p, 0, 0, 0, (100 - 64) * 8] == I.BF16_QNAN
+    pos, e = k_position(100 - 64, 3)
+    assert pool[0, p, 0, 0, pos * 8 + e] == I.BF16_QNAN
 
 
 def test_device_scatter_matches_host_layout():
     """The torch scatter used for full-size workloads writes the same layout."""
     w = I.Workload("t", seed=4, ctx_lens=[130, 64], num_layers=2, tile_tokens=64,
-                   num_q_heads=4, num_kv_heads=2, head_dim=8)
+                   num_q_heads=4, num_kv_heads=2, head_dim=256)
     t = I.draw_page_tables(w)
     pool_h, kv = I.host_pool(w, t, fill=0)
     pool_d = torch.zeros(pool_h.shape, dtype=torch.int16)
