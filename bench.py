@@ -25,6 +25,15 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 
+# Launch configuration timed for each workload (tile tokens; tokens per
+# work-group).  The full-size parity tests run exactly these.
+LAUNCH = {
+    "long262k": dict(tile=32768, split=4096),   # eight 32K staging tiles, split-KV inside
+    "conc": dict(tile=8192, split=2048),        # 8,192-token tiles per request
+    "mixed": dict(tile=8192, split=2048),
+    "tiny": dict(tile=1024, split=1024),
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -32,8 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long262k")
-    ap.add_argument("--tile", type=int, default=0, help="tile tokens (default: workload's)")
-    ap.add_argument("--split", type=int, default=0, help="tokens per work-group (0: library default)")
+    ap.add_argument("--tile", type=int, default=0, help="tile tokens (default: LAUNCH)")
+    ap.add_argument("--split", type=int, default=0, help="tokens per work-group (default: LAUNCH)")
     ap.add_argument("--kernel", default="mfma", choices=["mfma", "valu"])
     ap.add_argument("--staged", action="store_true",
                     help="decode each 32,768-token staging window with its own call")
@@ -60,10 +69,9 @@ def main():
     pkv.lib()
 
     w = I.workload(args.workload)
-    if args.workload == "long262k":
-        w.tile_tokens = 32768            # eight staging tiles, each split-KV inside
-    if args.tile:
-        w.tile_tokens = args.tile
+    launch = LAUNCH.get(args.workload, {})
+    w.tile_tokens = args.tile or launch.get("tile", w.tile_tokens)
+    args.split = args.split or launch.get("split", 0)
     T = w.tile_tokens
     B, Hq, Hkv, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
 

@@ -25,14 +25,22 @@
  *     lse = log sum_j exp(scale * q.k_j).
  *
  * Arena layout (one device allocation shared by every layer; GPU memory
- * management page, "Pages held by right, borrowed or free").  A physical
- * page holds page_tokens (64) consecutive tokens of one request for every
- * layer:
- *     arena[page][layer][K|V][kv_head][...]        (bf16)
- *     K block: token-major [64][head_dim]   (row = one token's key)
- *     V block: dim-major   [head_dim][64]   (row = one channel over 64 tokens)
- * so one (page, layer) is 2 * Hkv * 64 * head_dim * 2 bytes (256 KiB at
- * Hkv = 4, head_dim = 256) and one page is num_layers times that.
+ * management page, "Pages held by right, borrowed or free").  Physical page
+ * p holds page_tokens (64) consecutive tokens of one request, in every layer;
+ * the arena is layer-major so that one layer's pages form one slab:
+ *     arena[layer][page][K|V][kv_head][block]          (bf16)
+ * A block is 64 tokens x 256 channels (32 KiB) stored as 2,048 pieces of
+ * 16 bytes (8 bf16 values), in the order the decode kernel's wave loads
+ * consume them, 64 pieces (1 KiB) per load instruction:
+ *     K piece of token j, channels 8c..8c+7 is piece
+ *         ((h*2 + t)*8 + c/4)*64 + (c%4)*16 + r,
+ *         h = j/32, jj = j%32, t = (jj/4)%2, r = 4*(jj/8) + jj%4;
+ *     V piece of channel d, tokens 8u..8u+7 is piece
+ *         ((u/4)*16 + d/16)*64 + (u%4)*16 + d%16.
+ * One (layer, page) is 2 * Hkv blocks (256 KiB at Hkv = 4), one physical
+ * page num_layers times that, and a K+V token of one layer is
+ * 2 * Hkv * 256 * 2 = 4,096 bytes at Hkv = 4 (GPU memory management page,
+ * "A host pool that explains its own size").
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
 #ifndef PKV_H

@@ -1,0 +1,76 @@
+"""GPU parity at full workload sizes, in the launch configuration bench.py
+times (tile and split from bench.LAUNCH), on sampled layers that the float64
+oracle recomputes one by one; plus the staged-versus-resident bitwise gate
+over every layer of the 262K-token workload.
+
+Inputs come from the seeded device generator (torch's Philox); the oracle
+gets the same bf16 bits by regenerating each sampled layer."""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from paged_kv_cache_10_amd import inputs as I
+from gpu_helpers import Case, check_layer, same_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def full_case(name):
+    w = I.workload(name)
+    w.tile_tokens = bench.LAUNCH[name]["tile"]
+    return Case(w, host=False), bench.LAUNCH[name]["split"]
+
+
+@pytest.fixture(scope="module")
+def long262k(gpu):
+    case, split = full_case("long262k")
+    yield case, split
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_long262k_sampled_layers(long262k):
+    """1 x 262,144 tokens, 16 layers, 1 % boosted keys: layers 0, 7, 15 (all
+    24 heads, the 8 staging-tile partials and the merge) against the oracle."""
+    case, split = long262k
+    for layer in (0, 7, 15):
+        got = case.decode(layer, split=split)
+        err = check_layer(case, layer, got, case.oracle_layer(layer))
+        print(f"long262k layer {layer}: max abs err {err:.2e}")
+
+
+def test_long262k_staged_equals_resident_every_layer(long262k):
+    """Eight 32,768-token staged calls write the same bits as one resident
+    call, in all 16 layers (run-to-run agreement checked first)."""
+    case, split = long262k
+    for layer in range(case.w.num_layers):
+        a = case.decode(layer, split=split)
+        if layer == 0:
+            b = case.decode(layer, split=split)
+            assert all(same_bits(x, y) for x, y in zip(a, b))
+        c = case.decode(layer, split=split, staged=32768)
+        assert all(same_bits(x, y) for x, y in zip(a, c)), f"layer {layer}"
+
+
+def test_conc_sampled_layers(gpu):
+    """4 x 31,744 tokens, 16 layers, tile 8,192 (3 full tiles + 7,168)."""
+    case, split = full_case("conc")
+    for layer in (0, 15):
+        got = case.decode(layer, split=split)
+        err = check_layer(case, layer, got, case.oracle_layer(layer))
+        print(f"conc layer {layer}: max abs err {err:.2e}")
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_mixed_sampled_layers(gpu):
+    """16 requests, log-uniform lengths in [1,024, 131,072], 16 layers."""
+    case, split = full_case("mixed")
+    for layer in (3, 12):
+        got = case.decode(layer, split=split)
+        err = check_layer(case, layer, got, case.oracle_layer(layer))
+        print(f"mixed layer {layer}: max abs err {err:.2e}")
+    del case
+    torch.cuda.empty_cache()
