@@ -25,6 +25,37 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 
+# HBM traffic of one decode-kernel launch on the 262K workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+# scaled by the factor the same counter shows on a plain 1 GiB device copy
+# (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
+# Valid only for the kernel source it was measured on.
+PMC_TRAFFIC = {
+    "source_sha256": "72eeed38847317ba6b0903854fb79f1403c5bfe6495855baaf0ed858963f244a",
+    "workload": "long262k", "tile": 32768, "split": 4096,
+    "fetch_kib": 524443.5, "fetch_scale": 1048576 / 524306.0,
+    "write_kib": 1584.1, "write_scale": 1.0,
+}
+KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/device.h")
+
+
+def pmc_traffic(workload, tile, split, kernel):
+    """Counter-derived HBM bytes per launch, or None if they were not taken
+    on this kernel source and launch configuration."""
+    import hashlib
+    t = PMC_TRAFFIC
+    if (workload, tile, split, kernel) != (t["workload"], t["tile"], t["split"], "mfma"):
+        return None
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != t["source_sha256"]:
+        return None
+    return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+
+
 # Launch configuration timed for each workload (tile tokens; tokens per
 # work-group).  The full-size parity tests run exactly these.
 LAUNCH = {
@@ -51,6 +82,8 @@ def parse():
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy (the PMC calibration kernel)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="also report the measured HBM read ceiling (runs probe_read first)")
     return ap.parse_args()
 
 
@@ -60,6 +93,7 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(no multi-GPU path exists)", file=sys.stderr)
         return 2
+    ceiling = read_probe() if args.read_probe else None
     import torch
     from paged_kv_cache_10_amd import inputs as I
     from paged_kv_cache_10_amd import pkv
@@ -104,7 +138,7 @@ def main():
     lses = torch.empty((L, B, Hq), device=dev)
     window = 32768 if args.staged else span
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, window, T, D, args.kernel, args.split)
-    ws = torch.empty(max(16, ws_bytes) // 4 + 4, dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(16, ws_bytes) // 4 + 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def decode_layer(layer, ev=None):
@@ -183,10 +217,14 @@ def main():
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_ms": round(dec_avg_ms, 5),
-            "traffic": None,
+            "traffic": pmc_traffic(args.workload, T, args.split, args.kernel),
         },
         "setup_s": round(t_gen, 1),
     }
+
+    if ceiling is not None:
+        res["read_ceiling"] = ceiling
+        res["roofline"]["frac_of_measured_ceiling"] = round(dec_gbs / ceiling["blocks_GBs"], 4)
 
     if args.copy_probe:
         n = 1 << 29
@@ -211,6 +249,15 @@ def main():
 
     print(json.dumps(res), flush=True)
     return 0
+
+
+def read_probe():
+    """Measured HBM read ceiling: probe_read, run as a child process."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_10_amd",
+                       "probe_read")
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout
+    return json.loads(out.strip().splitlines()[-1])
 
 
 def cpu_baseline(w, qs, budget_s):

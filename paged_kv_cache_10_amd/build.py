@@ -2,6 +2,7 @@
 
     python -m paged_kv_cache_10_amd.build [--resource-usage]
 
+Also builds ``probe_read``, a standalone HBM read-ceiling probe.
 Every source is compiled by hipcc with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``), objects go to
 ``_build/`` and the shared library lands next to this file.
@@ -18,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+PROBE = os.path.join(HERE, "probe_read")          # HBM read-ceiling probe (an executable)
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "merge.hip", "decode_valu.hip", "decode_mfma.hip"]
@@ -67,6 +69,11 @@ def build(resource_usage=False, verbose=False):
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stdout}{p.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc()] + COMMON + [os.path.join(CSRC, "probe_read.hip"), "-o", PROBE + ".tmp"]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{p.stdout}{p.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     if verbose or resource_usage:
         for l in logs:
             print(l)

@@ -1,0 +1,143 @@
+// probe_read: HBM read-bandwidth ceiling of this GPU, for three load patterns.
+//
+// Measures what a streaming reader can reach on the box, so the decode
+// kernel's bytes-per-second can be set against a measured ceiling as well as
+// the 8 TB/s specification (the method of comparing bytes moved per launch
+// with a measured copy/read ceiling).  Reads a 1 GiB buffer:
+//   stream   grid-stride, each wave load instruction reads 1 KiB contiguous;
+//   blocks   32 KiB blocks in random order, one 4-wave work-group per CU
+//            (LDS reserved to hold occupancy at the decode kernel's), each
+//            load instruction 1 KiB contiguous: the decode kernel's pattern;
+//   rows     the same blocks, but each instruction reads 16 rows of 512 B at
+//            64 B per row (MFMA operand rows over token-major data).
+// Prints one JSON line.  Every load stays inside the buffer: indices are
+// bounded by construction and checked on the host before launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#define CHECK(x)                                                                  \
+  do {                                                                            \
+    hipError_t e_ = (x);                                                          \
+    if (e_ != hipSuccess) {                                                       \
+      fprintf(stderr, "probe_read: %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      exit(1);                                                                    \
+    }                                                                             \
+  } while (0)
+
+constexpr size_t kBytes = 1ull << 30;
+constexpr size_t kU4 = kBytes / 16;            // uint4 elements
+constexpr int kBlockU4 = 2048;                 // 32 KiB
+constexpr int kBlocks = (int)(kU4 / kBlockU4); // 32,768
+
+__global__ void stream_kernel(const uint4* __restrict__ p, uint32_t* out) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < kU4; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ b.y ^ c.z ^ d.w;
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+// wave w of a work-group takes blocks w, w+4, ...; `rows` selects the pattern
+template <bool kRows>
+__global__ void block_kernel(const uint4* __restrict__ p, const int* __restrict__ order,
+                             int per_wg, uint32_t* out) {
+  extern __shared__ uint32_t reserve[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t acc = 0;
+  for (int b = w; b < per_wg; b += 4) {
+    const uint4* blk = p + (size_t)order[blockIdx.x * per_wg + b] * kBlockU4;
+    uint4 v[32];
+    if (kRows) {
+      // 32 rows of 512 B (32 uint4); instruction (t, kb): rows 16t + lane%16, 64 B at kb
+      const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) v[t * 8 + kb] = blk[(16 * t + r) * 32 + 4 * kb + q];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) v[16 + t * 8 + kb] = blk[1024 + (16 * t + r) * 32 + 4 * kb + q];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = blk[j * 64 + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc ^= v[j].x ^ v[j].w;
+  }
+  if (acc == 0x9e3779b9u) {
+    reserve[0] = acc;
+    out[0] = reserve[threadIdx.x & 1];
+  }
+}
+
+int main() {
+  int dev = 0;
+  CHECK(hipSetDevice(dev));
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, dev));
+  const int cus = prop.multiProcessorCount;
+  uint4* p = nullptr;
+  uint32_t* out = nullptr;
+  int* order = nullptr;
+  CHECK(hipMalloc(&p, kBytes));
+  CHECK(hipMalloc(&out, 64));
+  CHECK(hipMemset(p, 1, kBytes));
+
+  const int nwg = cus;                          // one work-group per CU
+  const int per_wg = kBlocks / nwg;             // blocks per work-group
+  std::vector<int> h(kBlocks);
+  for (int i = 0; i < kBlocks; ++i) h[i] = i;
+  srand(7);
+  for (int i = kBlocks - 1; i > 0; --i) {
+    const int j = rand() % (i + 1);
+    const int t = h[i];
+    h[i] = h[j];
+    h[j] = t;
+  }
+  for (int i = 0; i < nwg * per_wg; ++i)
+    if (h[i] < 0 || h[i] >= kBlocks) { fprintf(stderr, "bad block index\n"); return 1; }
+  CHECK(hipMalloc(&order, sizeof(int) * kBlocks));
+  CHECK(hipMemcpy(order, h.data(), sizeof(int) * kBlocks, hipMemcpyHostToDevice));
+  const size_t lds = (size_t)prop.sharedMemPerMultiprocessor * 6 / 10;   // one WG per CU
+  const double bytes_blocks = (double)nwg * per_wg * kBlockU4 * 16;
+
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  auto time_it = [&](auto launch) {
+    for (int i = 0; i < 3; ++i) launch();
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    for (int i = 0; i < 20; ++i) launch();
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipGetLastError());
+    float ms = 0;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    return ms / 20.0;
+  };
+  const double ms_stream = time_it([&] {
+    hipLaunchKernelGGL(stream_kernel, dim3(2 * cus), dim3(256), 0, 0, p, out);
+  });
+  const double ms_blocks = time_it([&] {
+    hipLaunchKernelGGL(block_kernel<false>, dim3(nwg), dim3(256), lds, 0, p, order, per_wg, out);
+  });
+  const double ms_rows = time_it([&] {
+    hipLaunchKernelGGL(block_kernel<true>, dim3(nwg), dim3(256), lds, 0, p, order, per_wg, out);
+  });
+  printf("{\"device\": \"%s\", \"cus\": %d, \"bytes\": %zu, "
+         "\"stream_GBs\": %.1f, \"blocks_GBs\": %.1f, \"rows_GBs\": %.1f}\n",
+         prop.gcnArchName, cus, kBytes, kBytes / (ms_stream * 1e-3) / 1e9,
+         bytes_blocks / (ms_blocks * 1e-3) / 1e9, bytes_blocks / (ms_rows * 1e-3) / 1e9);
+  CHECK(hipFree(order));
+  CHECK(hipFree(out));
+  CHECK(hipFree(p));
+  return 0;
+}

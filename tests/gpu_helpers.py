@@ -89,7 +89,7 @@ class Case:
             po, pl, o, l = out
         window = span if staged is None else staged
         ws_bytes = pkv.decode_workspace_bytes(B, Hq, window, tile, D, kernel, split)
-        ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+        ws = torch.zeros(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device=DEV)
         for begin in range(0, span, window):
             count = min(window, span - begin)
             tab = self.dev_table[:, begin // w.page_tokens:]

@@ -151,3 +151,26 @@ def test_merge_identity_and_empty_insertion_bitwise(stress):
     got = merge(torch.cat(parts_o, 2).contiguous(), torch.cat(parts_l, 2).contiguous())
     for x, y in zip(ref, got):
         assert same_bits(x, y)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_workspace_reuse_across_calls(ragged, kernel):
+    """Tiles of 32 splits (2,048-token tiles of 64-token splits): three
+    back-to-back calls on one workspace give the same bits as a fresh
+    workspace each time."""
+    from paged_kv_cache_10_amd import pkv
+    w = ragged.w
+    tile, split = 2048, 64
+    S = ragged.num_slots(tile)
+    fresh = [ragged.decode(layer, tile=tile, kernel=kernel, split=split) for layer in (0, 1, 0)]
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    nbytes = pkv.decode_workspace_bytes(B, Hq, S * tile, tile, D, kernel, split)
+    ws = torch.zeros(nbytes // 4 + 4, device=DEV)
+    for layer, ref in zip((0, 1, 0), fresh):
+        po = torch.empty((B, Hq, S, D), device=DEV)
+        pl = torch.empty((B, Hq, S), device=DEV)
+        pkv.decode_attention(ragged.pool, layer, ragged.q[layer], ragged.dev_table, ragged.dev_ctx,
+                             0, S * tile, tile, w.scale, po, pl, workspace=ws, kernel=kernel,
+                             split_tokens=split)
+        torch.cuda.synchronize()
+        assert same_bits(po, ref[0]) and same_bits(pl, ref[1])
