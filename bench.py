@@ -2,11 +2,17 @@
 
 One step = one decode token for every request: for each of the 16 layers,
 pkv_decode_attention (split-KV tile partials) then pkv_merge_partials (FP32
-LSE merge).  Default workload: 1 request x 262,144 tokens, 16 layers, 24 q /
-4 KV heads, head_dim 256, bf16, 64-token pages in a 16 GiB arena in random
-physical order, 1 % of keys scaled by 4; the history is cut into eight
-32,768-token tiles, each split-KV inside, and all partials are merged in
-FP32.  Inputs are synthetic (seeded) and resident in HBM before timing.
+LSE merge); where LAUNCH says so, layer l's merge runs on a second stream
+while layer l+1 decodes, and the step ends when every merge has.  Default workload: 1 request x
+262,144 tokens, 16 layers, 24 q / 4 KV heads, head_dim 256, bf16, 64-token
+pages in a 16 GiB arena in random physical order, 1 % of keys scaled by 4;
+each 32,768-token staging window of the history is split-KV eight ways into
+4,096-token tiles and all 64 partials are merged in FP32.  Inputs are
+synthetic (seeded) and resident in HBM before timing.
+
+`value` comes from K steps timed with nothing but the path between two
+events; `roofline.achieved` from K further steps with an event pair around
+every pkv_decode_attention call.
 
 Prints one JSON line.  `value` is KV GB/s: K+V bytes the exact path must read
 per step (sum of lengths x 4,096 B x 16 layers) over the step time.
@@ -31,9 +37,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "72eeed38847317ba6b0903854fb79f1403c5bfe6495855baaf0ed858963f244a",
-    "workload": "long262k", "tile": 32768, "split": 4096,
-    "fetch_kib": 524443.5, "fetch_scale": 1048576 / 524306.0,
+    "source_sha256": "9e90796fc0fc87d52fbaed851b6ca443f42c3de1fa88af8dd1a8ce32b1c5e986",
+    "workload": "long262k", "tile": 4096, "split": 4096,
+    "fetch_kib": 524445.8, "fetch_scale": 1048576 / 524307.0,
     "write_kib": 1584.1, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/device.h")
@@ -58,11 +64,12 @@ def pmc_traffic(workload, tile, split, kernel):
 
 # Launch configuration timed for each workload (tile tokens; tokens per
 # work-group).  The full-size parity tests run exactly these.
+# `overlap`: layer l's merge runs on a second stream while layer l+1 decodes.
 LAUNCH = {
-    "long262k": dict(tile=32768, split=4096),   # eight 32K staging tiles, split-KV inside
-    "conc": dict(tile=8192, split=2048),        # 8,192-token tiles per request
-    "mixed": dict(tile=8192, split=2048),
-    "tiny": dict(tile=1024, split=1024),
+    "long262k": dict(tile=4096, split=4096, overlap=True),   # 32K windows split-KV 8 ways
+    "conc": dict(tile=8192, split=2048, overlap=False),      # 8,192-token tiles per request
+    "mixed": dict(tile=2048, split=2048, overlap=True),
+    "tiny": dict(tile=1024, split=1024, overlap=False),
 }
 
 
@@ -77,6 +84,7 @@ def parse():
     ap.add_argument("--kernel", default="mfma", choices=["mfma", "valu"])
     ap.add_argument("--staged", action="store_true",
                     help="decode each 32,768-token staging window with its own call")
+    ap.add_argument("--serial", action="store_true", help="merge on the decode stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
@@ -106,6 +114,7 @@ def main():
     launch = LAUNCH.get(args.workload, {})
     w.tile_tokens = args.tile or launch.get("tile", w.tile_tokens)
     args.split = args.split or launch.get("split", 0)
+    overlap = launch.get("overlap", False) and not args.serial
     T = w.tile_tokens
     B, Hq, Hkv, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
 
@@ -132,50 +141,79 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
-    po = torch.empty((B, Hq, slots, D), device=dev)
-    pl = torch.empty((B, Hq, slots), device=dev)
+    # per-layer partial buffers: layer l's merge (second stream) overlaps
+    # layer l+1's decode (main stream)
+    po = torch.empty((L, B, Hq, slots, D), device=dev)
+    pl = torch.empty((L, B, Hq, slots), device=dev)
     outs = torch.empty((L, B, Hq, D), device=dev)
     lses = torch.empty((L, B, Hq), device=dev)
     window = 32768 if args.staged else span
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, window, T, D, args.kernel, args.split)
     ws = torch.zeros(max(16, ws_bytes) // 4 + 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-
-    def decode_layer(layer, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        for begin in range(0, span, window):
-            pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc, begin,
-                                 min(window, span - begin), T, w.scale, po, pl, workspace=ws,
-                                 kernel=args.kernel, split_tokens=args.split, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        pkv.merge_partials(po, pl, outs[layer], lses[layer], stream=stream)
+    merge_stream = torch.cuda.Stream()          # default priority
+    decoded = [torch.cuda.Event() for _ in range(L)]
+    merged = torch.cuda.Event()
 
     def step(evs=None):
         for layer in range(L):
-            decode_layer(layer, None if evs is None else evs[layer])
+            if evs is not None:
+                evs[layer][0].record(stream)
+            for begin in range(0, span, window):
+                pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc,
+                                     begin, min(window, span - begin), T, w.scale, po[layer],
+                                     pl[layer], workspace=ws, kernel=args.kernel,
+                                     split_tokens=args.split, stream=stream)
+            if evs is not None:
+                evs[layer][1].record(stream)
+            if overlap:
+                decoded[layer].record(stream)
+                merge_stream.wait_event(decoded[layer])
+            pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer],
+                               stream=merge_stream if overlap else stream)
+        if overlap:
+            merged.record(merge_stream)
+            stream.wait_event(merged)              # the step ends when every merge has
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
+    # value: K steps with nothing but the path between two events
     K = args.steps
-    ev_dec = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(L)] for _ in range(K)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for k in range(K):
-        step(ev_dec[k])
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / K
+    ms_step = e0.elapsed_time(e1) / K
+    # roofline: K more steps with an event pair around every decode call
+    ev_dec = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)] for _ in range(K)]
+    for k in range(K):
+        step(ev_dec[k])
+    torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for evk in ev_dec for (a, b) in evk]
     dec_avg_ms = float(np.mean(dec_ms))
+
+    # the overlapped schedule against a serialized recompute on one stream
+    torch.cuda.synchronize()
+    ref_o, ref_l = outs.clone(), lses.clone()
+    for layer in range(L):
+        po[layer].fill_(float("nan"))
+        for begin in range(0, span, window):
+            pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc, begin,
+                                 min(window, span - begin), T, w.scale, po[layer], pl[layer],
+                                 workspace=ws, kernel=args.kernel, split_tokens=args.split,
+                                 stream=stream)
+        pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=stream)
+    torch.cuda.synchronize()
+    self_check = bool(torch.equal(ref_o.view(torch.int32), outs.view(torch.int32))
+                      and torch.equal(ref_l.view(torch.int32), lses.view(torch.int32)))
 
     kv_bytes_step = w.kv_bytes_per_step
     kv_gbs = kv_bytes_step / (ms_step * 1e-3) / 1e9
@@ -202,6 +240,7 @@ def main():
                         + (", staged 32768-token windows" if args.staged else ""),
             "batch": B, "ctx_lens_sum": int(sum(w.ctx_lens)), "layers": L, "tile_tokens": T,
             "kernel": args.kernel, "split_tokens": args.split or "default",
+            "merge_overlapped": overlap,
             "parallelism": "none (1 GPU)",
         },
         "tokens_per_s": round(tok_s, 2),
@@ -209,8 +248,9 @@ def main():
         "kv_bytes_per_step": kv_bytes_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "pkv_decode_attention (split-KV decode"
-                      + ("" if ws_bytes == 0 else " + tile finalize") + "), one layer per launch",
+            "kernel": "decode_mfma_kernel" if args.kernel == "mfma" else "decode_valu_kernel",
+            "launch": "one pkv_decode_attention call per layer = the decode kernel"
+                      + ("" if ws_bytes == 0 else " + the tile finalize"),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -220,6 +260,7 @@ def main():
             "traffic": pmc_traffic(args.workload, T, args.split, args.kernel),
         },
         "setup_s": round(t_gen, 1),
+        "overlapped_equals_serial_bitwise": self_check,
     }
 
     if ceiling is not None:

@@ -188,6 +188,16 @@ void decode_mfma_kernel(DecodeArgs a) {
   __shared__ float m_lds[kWaves][16];
   __shared__ float l_lds[kWaves][16];
 
+  // ---- a split with no key of the request: an empty partial, nothing read
+  if (t1 <= t0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      a.out_o[((row0 + h) * a.out_slots + slot) * D + tid] = 0.f;
+      if (tid == 0) a.out_lse[(row0 + h) * a.out_slots + slot] = -INFINITY;
+    }
+    return;
+  }
+
   // ---- stage the query group (zero rows past G)
   for (int i = tid; i < 16 * (D / 8); i += kThreads) {
     const int h = i / (D / 8);

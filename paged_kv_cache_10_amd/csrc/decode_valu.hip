@@ -64,6 +64,16 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int slot = a.out_slot0 + split;
   const int64_t row0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
 
+  // a split with no key of the request: an empty partial, nothing read
+  if (t1 <= t0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      a.out_o[((row0 + h) * a.out_slots + slot) * D + tid] = 0.f;
+      if (tid == 0) a.out_lse[(row0 + h) * a.out_slots + slot] = -INFINITY;
+    }
+    return;
+  }
+
   __shared__ float s_lds[G][PT];
   __shared__ float p_lds[kWaves][G][PT];
 
