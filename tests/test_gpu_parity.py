@@ -174,3 +174,30 @@ def test_workspace_reuse_across_calls(ragged, kernel):
                              split_tokens=split)
         torch.cuda.synchronize()
         assert same_bits(po, ref[0]) and same_bits(pl, ref[1])
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (48, 4), (64, 4), (16, 2)])
+def test_query_group_sizes(gpu, hq, hkv):
+    """Query groups of 1, 2, 4, 8, 12 and 16 heads per KV head (MFMA; the
+    VALU kernel up to 8), against the oracle, lengths around page edges."""
+    w = I.Workload("groups", seed=21, ctx_lens=[130, 2049, 777], num_layers=1,
+                   tile_tokens=1024, num_q_heads=hq, num_kv_heads=hkv)
+    case = Case(w, fill=I.BF16_QNAN)
+    ref = case.oracle_layer(0)
+    kernels = ["mfma"] + (["valu"] if hq // hkv <= 8 else [])
+    for kernel in kernels:
+        for split in (0, 256):
+            check_layer(case, 0, case.decode(0, kernel=kernel, split=split), ref)
+
+
+def test_one_million_tokens(gpu):
+    """One request of 1,048,576 tokens (one layer, 4 GiB of KV), 1 % of keys
+    scaled by 4, 4,096-token tiles: 256 partials per head merged in FP32."""
+    w = I.Workload("long1m", seed=31, ctx_lens=[1 << 20], num_layers=1, tile_tokens=4096,
+                   boost_frac=0.01)
+    case = Case(w, host=False)
+    got = case.decode(0, split=4096)
+    err = check_layer(case, 0, got, case.oracle_layer(0))
+    print(f"1M tokens: max abs err {err:.2e}")
+    del case
+    torch.cuda.empty_cache()
