@@ -194,6 +194,25 @@ int pkv_merge_partials(const float* part_out, const float* part_lse, int32_t row
                        int32_t num_slots, int32_t head_dim, float* out, float* lse,
                        void* stream);
 
+/* -------------------------------------------------------------- append --
+ * Write the new token of each request into its page of one layer, in the
+ * block layout above, so the next decode step attends over it (GPU memory
+ * management page, "Pages held by right, borrowed or free": the newest
+ * pages stay on the device).
+ *   dev_table      device int32 [batch][pt_stride], rows as for decode
+ *                  (entry i = logical page i of the request).
+ *   dev_positions  device int32 [batch]: the token index to write, normally
+ *                  the old length (the caller then passes length + 1 to
+ *                  decode); -1 skips a request.  A position whose page entry
+ *                  lies outside the row or outside [0, num_pages) is not
+ *                  written (never dereferenced); validated tables have none.
+ *   k_new, v_new   device bf16 [batch][num_kv_heads][256], 16-byte aligned.
+ * Only the 16-byte K pieces and 2-byte V elements of that token change; the
+ * rest of the page is untouched.  Queued on `stream`, no host wait. */
+int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
+                  int32_t pt_stride, const int32_t* dev_positions, int32_t batch,
+                  const void* k_new, const void* v_new, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -387,3 +387,33 @@ PKV_API int pkv_merge_partials(const float* part_out, const float* part_lse, int
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+PKV_API int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
+                          int32_t pt_stride, const int32_t* dev_positions, int32_t batch,
+                          const void* k_new, const void* v_new, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  const pkv_geom& G = pool->geom;
+  if (layer < 0 || layer >= G.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer = %d outside 0..%d", layer, G.num_layers - 1);
+  if (batch < 0 || batch > 65535) return fail(PKV_ERR_INVALID_ARG, "batch = %d outside 0..65535", batch);
+  if (pt_stride < 1) return fail(PKV_ERR_INVALID_ARG, "pt_stride = %d, need >= 1", pt_stride);
+  if (batch == 0) return ok();
+  if (!dev_table || !dev_positions || !k_new || !v_new)
+    return fail(PKV_ERR_INVALID_ARG, "dev_table, dev_positions, k_new or v_new is NULL");
+  if (reinterpret_cast<uintptr_t>(k_new) % 16)
+    return fail(PKV_ERR_INVALID_ARG, "k_new must be 16-byte aligned");
+  pkv::AppendArgs a;
+  a.arena = static_cast<uint16_t*>(pool->base);
+  a.page_elems = (int64_t)(pool->page_layer_bytes / 2);
+  a.layer_off = (int64_t)(pool->page_layer_bytes / 2) * pool->num_pages * layer;
+  a.num_pages = (int32_t)pool->num_pages;
+  a.num_kv_heads = G.num_kv_heads;
+  a.table = dev_table;
+  a.pt_stride = pt_stride;
+  a.positions = dev_positions;
+  a.k = static_cast<const uint16_t*>(k_new);
+  a.v = static_cast<const uint16_t*>(v_new);
+  hipError_t e = pkv::launch_append(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "append launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -30,6 +30,23 @@ hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int batch, int group, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int batch, int group, hipStream_t stream);
 
+// KV append: request b's token positions[b] gets rows k[b], v[b] of every KV
+// head in `layer`.
+struct AppendArgs {
+  uint16_t* arena;
+  int64_t page_elems;        // bf16 elements of one (layer, page)
+  int64_t layer_off;         // element offset of the layer's slab
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  const int32_t* table;      // [batch][pt_stride]
+  int32_t pt_stride;
+  const int32_t* positions;  // [batch] token index to write (-1: none)
+  const uint16_t* k;         // [batch][num_kv_heads][256] bf16
+  const uint16_t* v;         // [batch][num_kv_heads][256] bf16
+};
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
+
 // Largest query group each kernel supports.
 constexpr int kValuMaxGroup = 8;
 constexpr int kMfmaMaxGroup = 16;

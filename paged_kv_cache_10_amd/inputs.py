@@ -188,12 +188,15 @@ def boost_positions(w, layer, b, g, ctx):
 
 def draw_kv(w, layer, b):
     """Logical K and V of one request and layer: uint16 bf16 bits
-    [Hkv, ctx, D] each, token order 0..ctx-1."""
+    [Hkv, ctx, D] each, token order 0..ctx-1.  Each (layer, request, KV head)
+    has its own stream, drawn token by token, so a shorter history is a
+    prefix of a longer one (boosted positions aside)."""
     ctx = w.ctx_lens[b]
-    shape = (w.num_kv_heads, ctx, w.head_dim)
-    k = rng(w.seed, T_K, layer, b).standard_normal(shape, dtype=np.float32)
-    v = rng(w.seed, T_V, layer, b).standard_normal(shape, dtype=np.float32)
+    k = np.empty((w.num_kv_heads, ctx, w.head_dim), dtype=np.float32)
+    v = np.empty_like(k)
     for g in range(w.num_kv_heads):
+        k[g] = rng(w.seed, T_K, layer, b, g).standard_normal((ctx, w.head_dim), dtype=np.float32)
+        v[g] = rng(w.seed, T_V, layer, b, g).standard_normal((ctx, w.head_dim), dtype=np.float32)
         idx = boost_positions(w, layer, b, g, ctx)
         k[g, idx] *= 4.0                      # exact: a power of two
     return bf16_bits(k), bf16_bits(v)
@@ -295,21 +298,23 @@ def host_pool(w, table, layers=None, fill=0, pad_value=None):
 
 def device_kv(w, layer, b, device):
     """Logical K, V of one request and layer as torch bf16 [Hkv, ctx, D] on
-    `device`, from torch's Philox seeded by (seed, layer, request)."""
+    `device`, from torch's Philox seeded per (seed, layer, request, KV head)."""
     import torch
     ctx = w.ctx_lens[b]
-    shape = (w.num_kv_heads, ctx, w.head_dim)
-    gk = torch.Generator(device=device)
-    gk.manual_seed(seed64(w.seed, T_K, layer, b))
-    k = torch.randn(shape, generator=gk, device=device, dtype=torch.float32)
+    k = torch.empty((w.num_kv_heads, ctx, w.head_dim), dtype=torch.bfloat16, device=device)
+    v = torch.empty_like(k)
+    gen = torch.Generator(device=device)
     for g in range(w.num_kv_heads):
+        gen.manual_seed(seed64(w.seed, T_K, layer, b, g))
+        kf = torch.randn((ctx, w.head_dim), generator=gen, device=device, dtype=torch.float32)
         idx = boost_positions(w, layer, b, g, ctx)
         if len(idx):
-            k[g, torch.from_numpy(idx).to(device)] *= 4.0
-    k = k.to(torch.bfloat16)
-    gv = torch.Generator(device=device)
-    gv.manual_seed(seed64(w.seed, T_V, layer, b))
-    v = torch.randn(shape, generator=gv, device=device, dtype=torch.float32).to(torch.bfloat16)
+            kf[torch.from_numpy(idx).to(device)] *= 4.0
+        k[g] = kf.to(torch.bfloat16)
+        del kf
+        gen.manual_seed(seed64(w.seed, T_V, layer, b, g))
+        v[g] = torch.randn((ctx, w.head_dim), generator=gen, device=device,
+                           dtype=torch.float32).to(torch.bfloat16)
     return k, v
 
 

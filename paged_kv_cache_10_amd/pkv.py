@@ -25,6 +25,7 @@ EXPORTS = [
     "pkv_last_error", "pkv_abi_version", "pkv_page_bytes", "pkv_pool_create", "pkv_pool_info",
     "pkv_pool_destroy", "pkv_page_table_validate", "pkv_page_table_write",
     "pkv_decode_workspace_bytes", "pkv_decode_attention", "pkv_merge_partials",
+    "pkv_append_kv",
 ]
 
 
@@ -76,6 +77,7 @@ def lib():
                                            ctypes.c_float, P, P, I32, P, U64,
                                            ctypes.POINTER(DecodeOpts), P]
         L.pkv_merge_partials.argtypes = [P, P, I32, I32, I32, P, P, P]
+        L.pkv_append_kv.argtypes = [P, I32, P, I32, P, I32, P, P, P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -240,3 +242,21 @@ def merge_partials(part_out, part_lse, out, lse, stream=None):
         _ptr(part_out, torch.float32, "part_out"), _ptr(part_lse, torch.float32, "part_lse"),
         rows, S, D, _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
         _stream(stream)))
+
+
+def append_kv(pool, layer, dev_table, dev_positions, k_new, v_new, stream=None):
+    """Write token dev_positions[b] of request b (rows k_new[b], v_new[b]:
+    bf16 [B, Hkv, 256]) into its page of `layer`."""
+    import torch
+    B = k_new.shape[0]
+    if tuple(k_new.shape) != (B, pool.num_kv_heads, 256) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new and v_new must be [B, num_kv_heads, 256]")
+    if dev_table.dim() != 2 or dev_table.shape[0] != B or dev_table.stride(1) != 1:
+        raise ValueError("dev_table must be [B, pt_stride] with contiguous rows")
+    if dev_positions.numel() != B:
+        raise ValueError("dev_positions must have B entries")
+    _check(lib().pkv_append_kv(pool.handle, int(layer), dev_table.data_ptr(),
+                               int(dev_table.stride(0)),
+                               _ptr(dev_positions, torch.int32, "dev_positions"), B,
+                               _ptr(k_new, torch.bfloat16, "k_new"),
+                               _ptr(v_new, torch.bfloat16, "v_new"), _stream(stream)))

@@ -196,3 +196,20 @@ def test_empty_calls_do_nothing():
     # batch 0 or an empty window validate and return without launching
     assert decode_raw(FakePool(64), batch=0)[0] == 0
     assert decode_raw(FakePool(64), count=0)[0] == 0
+
+
+def test_append_arguments_are_refused_on_the_host():
+    L = pkv.lib()
+    pool = FakePool(8)
+    args = dict(layer=0, table=1 << 20, stride=4, pos=1 << 21, batch=2, k=1 << 22, v=1 << 23)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.pkv_append_kv(pool.handle, a["layer"], a["table"], a["stride"], a["pos"],
+                               a["batch"], a["k"], a["v"], None), err()
+    for kw, needle in [(dict(layer=16), "layer"), (dict(batch=-1), "batch"),
+                       (dict(stride=0), "pt_stride"), (dict(k=None), "NULL"),
+                       (dict(k=(1 << 22) + 2), "aligned")]:
+        rc, msg = call(**kw)
+        assert rc == -1 and needle in msg, (kw, msg)
+    assert call(batch=0)[0] == 0

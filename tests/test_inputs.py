@@ -142,3 +142,15 @@ def test_stress_draws_forced_rows():
     assert d["empty"][0, 0].all()
     assert (~d["empty"][0, 1]).sum() == 1
     assert d["target_lse"].min() >= -40 and d["target_lse"].max() <= 40
+
+
+def test_shorter_history_is_a_prefix():
+    """Per-head streams: the K/V of a shorter history are the first rows of a
+    longer one, which is what lets an appended token be checked bit for bit."""
+    w = I.Workload("p", seed=8, ctx_lens=[70], num_layers=2, tile_tokens=64)
+    w2 = I.Workload("p", seed=8, ctx_lens=[71], num_layers=2, tile_tokens=64)
+    for layer in range(2):
+        k, v = I.draw_kv(w, layer, 0)
+        k2, v2 = I.draw_kv(w2, layer, 0)
+        np.testing.assert_array_equal(k, k2[:, :70])
+        np.testing.assert_array_equal(v, v2[:, :70])
