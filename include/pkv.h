@@ -60,7 +60,10 @@ enum {
   PKV_ERR_WORKSPACE = -4,        /* workspace missing or smaller than pkv_decode_workspace_bytes */
   PKV_ERR_PAGE_TABLE = -5,       /* a page-table row the pool cannot serve */
   PKV_ERR_LAUNCH = -6,           /* the HIP runtime refused a launch */
-  PKV_ERR_DEVICE = -7            /* a HIP runtime call (copy, device query) failed */
+  PKV_ERR_DEVICE = -7,           /* a HIP runtime call (copy, device query) failed */
+  PKV_ERR_LEASE = -8,            /* a lease call out of order (see the stager below) */
+  PKV_ERR_BUSY = -9,             /* leases outstanding: retire before destroying */
+  PKV_ERR_QUARANTINED = -10      /* the stager saw a failure; only retire is accepted */
 };
 
 /* Geometry of the arena.  The kernels are built for head_dim = 256,
@@ -203,7 +206,9 @@ int pkv_merge_partials(const float* part_out, const float* part_lse, int32_t row
  *                  (entry i = logical page i of the request).
  *   dev_positions  device int32 [batch]: the token index to write, normally
  *                  the old length (the caller then passes length + 1 to
- *                  decode); -1 skips a request.  A position whose page entry
+ *                  decode), counted from the first logical page of the row
+ *                  (with a lease's staging table: minus window_begin); -1
+ *                  skips a request.  A position whose page entry
  *                  lies outside the row or outside [0, num_pages) is not
  *                  written (never dereferenced); validated tables have none.
  *   k_new, v_new   device bf16 [batch][num_kv_heads][256], 16-byte aligned.
@@ -212,6 +217,70 @@ int pkv_merge_partials(const float* part_out, const float* part_lse, int32_t row
 int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
                   int32_t pt_stride, const int32_t* dev_positions, int32_t batch,
                   const void* k_new, const void* v_new, void* stream);
+
+/* ---------------------------------------------------------- staged tiles --
+ * History held in pinned host memory, brought to the device one window of
+ * one layer at a time under a lease (Staging without a stall, sections "Two
+ * copy queues and device-side ordering" and "Leases instead of buffers";
+ * KV-cache engineering, "Staging layers under a lease"; GPU memory
+ * management, "Staging as a lease").
+ *
+ * The host arena has the layout of a pool with `host_layers` layers and the
+ * staging pool's head shape: host[layer][page][K|V][kv_head][block].  The
+ * stager owns `num_buffers` staging buffers in layer 0 of the staging pool,
+ * each of max_batch x window_tokens/64 pages, and three caller streams:
+ *   copy       host -> device window copies;
+ *   compute    the caller's work on a lease (decode, append) runs here;
+ *   writeback  device -> host copies of changed tail pages.
+ * Ordering is on the device: a window's copy waits for the previous readers
+ * of the buffer it overwrites (that lease's consumer and write-back events),
+ * the compute stream waits for the copy, and the write-back waits for the
+ * compute stream's consumer event.  Only pkv_stager_retire blocks the host.
+ *
+ * Lifecycle.  pkv_lease_begin queues the copy of tokens
+ * [window_begin, window_begin + window_tokens) of every request (runs of
+ * consecutive host pages in one copy each) and fills *lease: the staging
+ * table (entry i of row b = logical page window_begin/64 + i) to pass to
+ * pkv_decode_attention / pkv_append_kv with the staging pool and
+ * lease.staging_layer, on the compute stream.  pkv_lease_seal records the
+ * consumer event after that work and, if write_back_tail, copies back the
+ * pages holding each request's last token (ctx_lens[b] - 1) when they lie in
+ * the window.  A new lease may begin only after the previous one is sealed;
+ * a seal must name the open lease.  Stage generations only increase.
+ * pkv_stager_retire waits for every sealed lease and returns their count as
+ * receipts.  Any HIP failure quarantines the stager: begin and seal are
+ * refused, retire drains the copy, write-back and compute streams and the
+ * device, and if a drain fails everything stays retained.  Destroy never
+ * waits: with leases outstanding it refuses (PKV_ERR_BUSY).
+ * dev_tables is device int32 [num_buffers][max_batch][window_tokens/64],
+ * written once by create.  The host arena and staging pool must outlive the
+ * stager. */
+typedef struct pkv_stager pkv_stager;
+typedef struct pkv_lease {
+  uint64_t generation;      /* stage generation, 1, 2, ... per stager          */
+  int32_t layer;            /* host layer staged                               */
+  int32_t window_begin;     /* first token of the window                       */
+  int32_t buffer;           /* staging buffer used                             */
+  int32_t staging_layer;    /* layer of the staging pool to decode from (0)    */
+  const int32_t* dev_table; /* staging page table, rows of pt_stride entries   */
+  int32_t pt_stride;        /* window_tokens / 64                              */
+} pkv_lease;
+
+int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_t host_bytes,
+                      int32_t host_layers, int32_t max_batch, int32_t window_tokens,
+                      int32_t num_buffers, int32_t* dev_tables, void* copy_stream,
+                      void* compute_stream, void* writeback_stream, pkv_stager** out);
+int pkv_lease_begin(pkv_stager* stager, int32_t layer, const int32_t* host_table,
+                    int32_t pt_stride, const int32_t* host_ctx_lens, int32_t batch,
+                    int32_t window_begin, pkv_lease* lease);
+int pkv_lease_seal(pkv_stager* stager, const pkv_lease* lease, int32_t write_back_tail);
+int pkv_stager_retire(pkv_stager* stager, int64_t* receipts);
+int pkv_stager_info(const pkv_stager* stager, uint64_t* generation, int64_t* unretired,
+                    int32_t* open, int32_t* quarantined);
+/* Mark the transport failed from the caller's side (its own work on a lease
+ * failed): the stager is quarantined exactly as after a HIP failure. */
+int pkv_stager_fail(pkv_stager* stager);
+int pkv_stager_destroy(pkv_stager* stager);
 
 #ifdef __cplusplus
 }

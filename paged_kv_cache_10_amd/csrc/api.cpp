@@ -10,34 +10,38 @@
 #include <new>
 #include <vector>
 
-#include "../../include/pkv.h"
 #include "kernels.h"
+#include "pool.h"
 
 #define PKV_API extern "C" __attribute__((visibility("default")))
 
-struct pkv_pool {
-  pkv_geom geom;
-  void* base;
-  uint64_t bytes;
-  uint64_t page_bytes;        // one physical page, all layers
-  uint64_t page_layer_bytes;  // one (page, layer)
-  int64_t num_pages;
-};
-
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+namespace pkv {
+int set_error(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
   return code;
 }
+void clear_error() { g_err[0] = '\0'; }
+}  // namespace pkv
+
+namespace {
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wformat-security"
+template <typename... A>
+int fail(int code, const char* fmt, A... args) {   // every caller passes a literal
+  return pkv::set_error(code, fmt, args...);
+}
+#pragma clang diagnostic pop
 
 int ok() {
-  g_err[0] = '\0';
+  pkv::clear_error();
   return PKV_OK;
 }
 

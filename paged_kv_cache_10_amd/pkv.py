@@ -17,6 +17,7 @@ PKV_OK = 0
 ERRORS = {
     -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_AUTO_SIZE_REFUSED", -3: "PKV_ERR_GEOMETRY",
     -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_PAGE_TABLE", -6: "PKV_ERR_LAUNCH", -7: "PKV_ERR_DEVICE",
+    -8: "PKV_ERR_LEASE", -9: "PKV_ERR_BUSY", -10: "PKV_ERR_QUARANTINED",
 }
 KERNELS = {"default": 0, "valu": 1, "mfma": 2}
 
@@ -25,7 +26,8 @@ EXPORTS = [
     "pkv_last_error", "pkv_abi_version", "pkv_page_bytes", "pkv_pool_create", "pkv_pool_info",
     "pkv_pool_destroy", "pkv_page_table_validate", "pkv_page_table_write",
     "pkv_decode_workspace_bytes", "pkv_decode_attention", "pkv_merge_partials",
-    "pkv_append_kv",
+    "pkv_append_kv", "pkv_stager_create", "pkv_lease_begin", "pkv_lease_seal",
+    "pkv_stager_retire", "pkv_stager_info", "pkv_stager_fail", "pkv_stager_destroy",
 ]
 
 
@@ -43,6 +45,13 @@ class Geom(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32)]
+
+
+class Lease(ctypes.Structure):
+    _fields_ = [("generation", ctypes.c_uint64), ("layer", ctypes.c_int32),
+                ("window_begin", ctypes.c_int32), ("buffer", ctypes.c_int32),
+                ("staging_layer", ctypes.c_int32), ("dev_table", ctypes.c_void_p),
+                ("pt_stride", ctypes.c_int32)]
 
 
 _lib = None
@@ -78,6 +87,15 @@ def lib():
                                            ctypes.POINTER(DecodeOpts), P]
         L.pkv_merge_partials.argtypes = [P, P, I32, I32, I32, P, P, P]
         L.pkv_append_kv.argtypes = [P, I32, P, I32, P, I32, P, P, P]
+        L.pkv_stager_create.argtypes = [P, P, U64, I32, I32, I32, I32, P, P, P, P,
+                                        ctypes.POINTER(P)]
+        L.pkv_lease_begin.argtypes = [P, I32, I32P, I32, I32P, I32, I32, ctypes.POINTER(Lease)]
+        L.pkv_lease_seal.argtypes = [P, ctypes.POINTER(Lease), I32]
+        L.pkv_stager_retire.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.pkv_stager_info.argtypes = [P, ctypes.POINTER(U64), ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        L.pkv_stager_destroy.argtypes = [P]
+        L.pkv_stager_fail.argtypes = [P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -260,3 +278,67 @@ def append_kv(pool, layer, dev_table, dev_positions, k_new, v_new, stream=None):
                                _ptr(dev_positions, torch.int32, "dev_positions"), B,
                                _ptr(k_new, torch.bfloat16, "k_new"),
                                _ptr(v_new, torch.bfloat16, "v_new"), _stream(stream)))
+
+
+class Stager:
+    """Staged tiles under a lease (pkv_stager_*): history in pinned host
+    memory `host_arena` (a pinned tensor in pool layout with `host_layers`
+    layers), staging buffers in layer 0 of `staging_pool`."""
+
+    def __init__(self, staging_pool, host_arena, host_layers, max_batch, window_tokens,
+                 num_buffers, copy_stream, compute_stream, writeback_stream):
+        import torch
+        if not host_arena.is_pinned():
+            raise ValueError("host_arena must be pinned host memory")
+        self.pool = staging_pool
+        self.host_arena = host_arena
+        self.max_batch = max_batch
+        self.window_pages = window_tokens // 64
+        self.num_buffers = num_buffers
+        self.streams = (copy_stream, compute_stream, writeback_stream)
+        self.dev_tables = torch.empty((num_buffers, max_batch, self.window_pages),
+                                      dtype=torch.int32, device="cuda")
+        h = P()
+        _check(lib().pkv_stager_create(
+            staging_pool.handle, host_arena.data_ptr(),
+            host_arena.numel() * host_arena.element_size(), host_layers, max_batch,
+            window_tokens, num_buffers, self.dev_tables.data_ptr(), _stream(copy_stream),
+            _stream(compute_stream), _stream(writeback_stream), ctypes.byref(h)))
+        self.handle = h
+
+    def begin(self, layer, host_table, host_ctx_lens, window_begin):
+        """Queue the window's copy; returns the Lease."""
+        t, tp = _i32_array(host_table)
+        c, cp = _i32_array(host_ctx_lens)
+        lease = Lease()
+        _check(lib().pkv_lease_begin(self.handle, int(layer), tp, t.shape[1], cp, t.shape[0],
+                                     int(window_begin), ctypes.byref(lease)))
+        lease.batch = t.shape[0]
+        return lease
+
+    def table(self, lease):
+        """The lease's staging page table as a device tensor [batch, pt_stride]."""
+        return self.dev_tables[lease.buffer, :lease.batch]
+
+    def seal(self, lease, write_back_tail=False):
+        _check(lib().pkv_lease_seal(self.handle, ctypes.byref(lease), int(bool(write_back_tail))))
+
+    def retire(self):
+        n = ctypes.c_int64()
+        _check(lib().pkv_stager_retire(self.handle, ctypes.byref(n)))
+        return n.value
+
+    def info(self):
+        g, u, o, q = U64(), ctypes.c_int64(), I32(), I32()
+        _check(lib().pkv_stager_info(self.handle, ctypes.byref(g), ctypes.byref(u),
+                                     ctypes.byref(o), ctypes.byref(q)))
+        return dict(generation=g.value, unretired=u.value, open=bool(o.value),
+                    quarantined=bool(q.value))
+
+    def fail(self):
+        _check(lib().pkv_stager_fail(self.handle))
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            _check(lib().pkv_stager_destroy(self.handle))
+            self.handle = None
