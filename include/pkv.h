@@ -282,6 +282,61 @@ int pkv_stager_info(const pkv_stager* stager, uint64_t* generation, int64_t* unr
 int pkv_stager_fail(pkv_stager* stager);
 int pkv_stager_destroy(pkv_stager* stager);
 
+/* ------------------------------------------------------------ admission --
+ * Which logical pages of which contexts hold device pages, decided at step
+ * boundaries by explicit arithmetic (Staging without a stall, section
+ * "Admission that does arithmetic"; GPU memory management, section "Pages
+ * held by right, borrowed or free").  Host only: no device memory is touched
+ * and no HIP call is made.  Device page ids are 0..num_pages-1 of a pool of
+ * that explicit size (0 is refused).
+ *
+ * A context holds its sink page (logical page 0) and its newest pages:
+ * `target` pages by right plus up to `burst` borrowed while pages are free;
+ * its floor is the sink plus one page.  pkv_admit_step takes the contexts
+ * active in this step, in priority order, with their lengths in tokens, and
+ * for each fills the sink and then the newest pages downward.  A missing
+ * page comes from, in order: (1) the context's own page outside its window,
+ * (2) a free page (marked borrowed once the context holds its target),
+ * (3) while below target, other contexts least recently active first: their
+ * borrowed pages, then pages above their target, then whole idle contexts,
+ * (4) the context's own oldest non-sink page older than the one wanted.  If
+ * none exists the context is refused for the step when it lacks its sink or
+ * floor; otherwise its window stays shorter and the rest is staged.
+ *   table   int32 [n][pt_stride] out: device page of each logical page, -1
+ *           where the page is not resident (to be staged from the host).
+ *   status  int32 [n] out: PKV_ADMIT_FULL, PKV_ADMIT_PARTIAL or
+ *           PKV_ADMIT_REFUSED_STEP.
+ * Every fill and reclamation is counted (pkv_admit_get_counts) and logged
+ * (pkv_admit_events drains the log). */
+enum {
+  PKV_ADMIT_REUSE_OWN = 1, PKV_ADMIT_TAKE_FREE = 2, PKV_ADMIT_RECLAIM_BORROWED = 3,
+  PKV_ADMIT_RECLAIM_ABOVE_TARGET = 4, PKV_ADMIT_RECLAIM_IDLE = 5, PKV_ADMIT_SHRINK_OWN = 6,
+  PKV_ADMIT_REFUSED = 7
+};
+enum { PKV_ADMIT_FULL = 0, PKV_ADMIT_PARTIAL = 1, PKV_ADMIT_REFUSED_STEP = 2 };
+typedef struct pkv_admit pkv_admit;
+typedef struct pkv_admit_counts {
+  int64_t steps, reuse_own, take_free, reclaim_borrowed, reclaim_above_target, reclaim_idle,
+      shrink_own, refused, free_pages;
+} pkv_admit_counts;
+typedef struct pkv_admit_event {
+  int64_t step;      /* step number (1, 2, ...)                                  */
+  int32_t kind;      /* PKV_ADMIT_REUSE_OWN .. PKV_ADMIT_REFUSED                 */
+  int32_t context;   /* the context served (or refused)                          */
+  int32_t victim;    /* context the page came from; -1 for the free list        */
+  int32_t page;      /* device page; -1 for a whole-context eviction or refusal */
+  int32_t logical;   /* logical page it now holds; -1 if none                    */
+} pkv_admit_event;
+int pkv_admit_create(int64_t num_pages, int32_t page_tokens, pkv_admit** out);
+int pkv_admit_add(pkv_admit* a, int32_t ctx, int32_t target_pages, int32_t burst_pages);
+int pkv_admit_set_target(pkv_admit* a, int32_t ctx, int32_t target_pages, int32_t burst_pages);
+int pkv_admit_remove(pkv_admit* a, int32_t ctx);
+int pkv_admit_step(pkv_admit* a, int32_t n, const int32_t* ctx_ids, const int64_t* lengths,
+                   int32_t* table, int32_t pt_stride, int32_t* status);
+int pkv_admit_get_counts(const pkv_admit* a, pkv_admit_counts* out);
+int pkv_admit_events(pkv_admit* a, pkv_admit_event* out, int32_t cap, int32_t* n_out);
+int pkv_admit_destroy(pkv_admit* a);
+
 #ifdef __cplusplus
 }
 #endif

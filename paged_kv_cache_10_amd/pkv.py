@@ -28,6 +28,8 @@ EXPORTS = [
     "pkv_decode_workspace_bytes", "pkv_decode_attention", "pkv_merge_partials",
     "pkv_append_kv", "pkv_stager_create", "pkv_lease_begin", "pkv_lease_seal",
     "pkv_stager_retire", "pkv_stager_info", "pkv_stager_fail", "pkv_stager_destroy",
+    "pkv_admit_create", "pkv_admit_add", "pkv_admit_set_target", "pkv_admit_remove",
+    "pkv_admit_step", "pkv_admit_get_counts", "pkv_admit_events", "pkv_admit_destroy",
 ]
 
 
@@ -45,6 +47,22 @@ class Geom(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32)]
+
+
+class AdmitCounts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "steps", "reuse_own", "take_free", "reclaim_borrowed", "reclaim_above_target",
+        "reclaim_idle", "shrink_own", "refused", "free_pages")]
+
+
+class AdmitEvent(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("kind", ctypes.c_int32), ("context", ctypes.c_int32),
+                ("victim", ctypes.c_int32), ("page", ctypes.c_int32), ("logical", ctypes.c_int32)]
+
+
+ADMIT_KINDS = {1: "reuse_own", 2: "take_free", 3: "reclaim_borrowed", 4: "reclaim_above_target",
+               5: "reclaim_idle", 6: "shrink_own", 7: "refused"}
+ADMIT_STATUS = {0: "full", 1: "partial", 2: "refused"}
 
 
 class Lease(ctypes.Structure):
@@ -96,6 +114,15 @@ def lib():
                                       ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.pkv_stager_destroy.argtypes = [P]
         L.pkv_stager_fail.argtypes = [P]
+        I64P = ctypes.POINTER(ctypes.c_int64)
+        L.pkv_admit_create.argtypes = [ctypes.c_int64, I32, ctypes.POINTER(P)]
+        L.pkv_admit_add.argtypes = [P, I32, I32, I32]
+        L.pkv_admit_set_target.argtypes = [P, I32, I32, I32]
+        L.pkv_admit_remove.argtypes = [P, I32]
+        L.pkv_admit_step.argtypes = [P, I32, I32P, I64P, I32P, I32, I32P]
+        L.pkv_admit_get_counts.argtypes = [P, ctypes.POINTER(AdmitCounts)]
+        L.pkv_admit_events.argtypes = [P, ctypes.POINTER(AdmitEvent), I32, ctypes.POINTER(I32)]
+        L.pkv_admit_destroy.argtypes = [P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -342,3 +369,64 @@ class Stager:
         if getattr(self, "handle", None):
             _check(lib().pkv_stager_destroy(self.handle))
             self.handle = None
+
+
+class Admission:
+    """Host-side device page admission (pkv_admit_*)."""
+
+    def __init__(self, num_pages, page_tokens=64):
+        h = P()
+        _check(lib().pkv_admit_create(int(num_pages), int(page_tokens), ctypes.byref(h)))
+        self.handle = h
+        self.num_pages = num_pages
+
+    def add(self, ctx, target, burst=0):
+        _check(lib().pkv_admit_add(self.handle, ctx, target, burst))
+
+    def set_target(self, ctx, target, burst=0):
+        _check(lib().pkv_admit_set_target(self.handle, ctx, target, burst))
+
+    def remove(self, ctx):
+        _check(lib().pkv_admit_remove(self.handle, ctx))
+
+    def step(self, ctx_ids, lengths, pt_stride):
+        """Returns (table int32 [n, pt_stride], status list of 'full' /
+        'partial' / 'refused')."""
+        import numpy as np
+        ids, idp = _i32_array(ctx_ids)
+        ln = np.ascontiguousarray(lengths, dtype=np.int64)
+        n = len(ids)
+        table = np.empty((max(n, 1), pt_stride), dtype=np.int32)
+        status = np.empty(max(n, 1), dtype=np.int32)
+        _check(lib().pkv_admit_step(self.handle, n, idp,
+                                    ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    table.ctypes.data_as(I32P), pt_stride,
+                                    status.ctypes.data_as(I32P)))
+        return table[:n], [ADMIT_STATUS[int(x)] for x in status[:n]]
+
+    def counts(self):
+        c = AdmitCounts()
+        _check(lib().pkv_admit_get_counts(self.handle, ctypes.byref(c)))
+        return {n: getattr(c, n) for n, _ in AdmitCounts._fields_}
+
+    def events(self):
+        out = []
+        buf = (AdmitEvent * 256)()
+        while True:
+            n = I32()
+            _check(lib().pkv_admit_events(self.handle, buf, 256, ctypes.byref(n)))
+            out += [dict(step=e.step, kind=ADMIT_KINDS[e.kind], context=e.context,
+                         victim=e.victim, page=e.page, logical=e.logical) for e in buf[:n.value]]
+            if n.value < 256:
+                return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().pkv_admit_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
