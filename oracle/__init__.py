@@ -15,10 +15,16 @@ tiles by exp(lse_t - max lse), divides by the summed weights and reports
 max + log(sum) as the merged log-sum-exp.  The merged result is softmax
 attention over the union of all keys.
 
+The compact representation of older pages (same page and section: runs of
+two representations, a page converted once fully written, with a CRC) is in
+``compact``: E4M3 codes with one FP32 scale per block, dequantisation,
+CRC-32 and an error bound for the log-sum-exp.
+
 Every function here is pinned by ``tests/test_oracle.py`` against things
 other than itself: brute force with exact summation, library routines
 (torch's scaled-dot-product attention, scipy's logsumexp), closed forms,
-hand-derived golden fixtures and planted mistakes.
+hand-derived golden fixtures and planted mistakes; ``compact`` by
+``tests/test_oracle_compact.py``.
 """
 
 from .attention import (  # noqa: F401
@@ -33,3 +39,4 @@ from .attention import (  # noqa: F401
     stress_partials,
     union_attention,
 )
+from . import compact  # noqa: F401
