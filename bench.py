@@ -73,6 +73,16 @@ LAUNCH = {
 }
 
 
+# Runs of two representations (--compact-older): every page older than the
+# newest `exact_tail` tokens is served from compact (E4M3) pages.  The
+# compact run's split gives 256 work-groups at 262K (3,584 tokens x 64
+# splits x 4 KV heads), the exact tail's 512-token splits also 256.  The
+# full-size compact parity test runs exactly these.
+COMPACT_LAUNCH = {
+    "long262k": dict(exact_tail=32768, tile=3584, split=3584, exact_tile=512, exact_split=512),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +97,9 @@ def parse():
     ap.add_argument("--serial", action="store_true", help="merge on the decode stream")
     ap.add_argument("--host-staged", action="store_true",
                     help="history in pinned host memory, staged per 32K window under leases")
+    ap.add_argument("--compact-older", action="store_true",
+                    help="serve pages older than the newest 32,768 tokens from compact (E4M3) "
+                         "pages converted on the GPU; prints its own JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
@@ -219,6 +232,10 @@ def main():
 
     if args.host_staged:
         res = host_staged(args, w, pool, arena, table, ctx, qs, outs, lses, T, span)
+        print(json.dumps(res), flush=True)
+        return 0
+    if args.compact_older:
+        res = compact_older(args, w, pool, table, ctx, qs, outs, lses)
         print(json.dumps(res), flush=True)
         return 0
 
@@ -404,6 +421,143 @@ def host_staged(args, w, pool, arena, table, ctx, qs, ref_outs, ref_lses, T, spa
                      "peak": round(h2d_ceiling, 2), "unit": "GB/s",
                      "frac": round(copied / (ms * 1e-3) / 1e9 / h2d_ceiling, 4),
                      "peak_kind": "measured: plain 1 GiB pinned-to-device copy"},
+    }
+
+
+def compact_older(args, w, pool, table, ctx, qs, ref_outs, ref_lses):
+    """Runs of two representations: each request's pages older than its
+    newest exact_tail tokens are converted on the GPU into compact (E4M3)
+    pages with their CRC and decoded from there; the tail stays exact; the
+    two runs write disjoint slots and one FP32 merge combines them."""
+    import torch
+    from paged_kv_cache_10_amd import pkv
+    dev = qs[0].device
+    cl = COMPACT_LAUNCH[w.name]
+    L, B, Hq, Hkv, D = w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    PT = w.page_tokens
+    c = np.array([max(0, (n - cl["exact_tail"]) // PT * PT) for n in w.ctx_lens], np.int32)
+    npc = c // PT
+    P = int(npc.sum())
+    cpb = pkv.compact_page_bytes(L, Hkv)
+    carena = torch.zeros(P * cpb, dtype=torch.uint8, device=dev)
+    cpool = pkv.Pool(carena, L, Hkv, compact=True)
+    ids = np.random.default_rng(w.seed + 7).permutation(P).astype(np.int32)
+    width = table.shape[1]
+    ctab = np.full((B, width), -1, np.int32)
+    etab = np.full((B, width), -1, np.int32)
+    src, k = [], 0
+    for b in range(B):
+        ctab[b, :npc[b]] = ids[k:k + npc[b]]
+        src.extend(table[b, :npc[b]].tolist())
+        k += npc[b]
+        rest = table[b, npc[b]:]
+        rest = rest[rest >= 0]
+        etab[b, :rest.size] = rest
+    ectx = (ctx - c).astype(np.int32)
+    dct, dcc = torch.empty((B, width), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev)
+    det, dec = torch.empty((B, width), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev)
+    pkv.page_table_write(cpool, ctab, c, dct, dcc)
+    pkv.page_table_write(pool, etab, ectx, det, dec)
+    dsrc = torch.tensor(src, dtype=torch.int32, device=dev)
+    ddst = torch.tensor(ids[:P], dtype=torch.int32, device=dev)
+    crc = torch.empty(P, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pkv.compact_convert(pool, cpool, dsrc, ddst, crc)          # warm
+    torch.cuda.synchronize()
+    e0.record(stream)
+    pkv.compact_convert(pool, cpool, dsrc, ddst, crc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    convert_ms = e0.elapsed_time(e1)
+    crc_host = crc.cpu().numpy().view(np.uint32)
+    again = torch.empty_like(crc)
+    pkv.compact_crc(cpool, ddst, again)
+    torch.cuda.synchronize()
+    crc_ok = bool(np.array_equal(crc_host, again.cpu().numpy().view(np.uint32)))
+
+    T, S, Te, Se_ = cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"]
+    Sc = max(1, -(-int(c.max()) // T))
+    Se = max(1, -(-int(ectx.max()) // Te))
+    po = torch.empty((L, B, Hq, Sc + Se, D), device=dev)
+    pl = torch.empty((L, B, Hq, Sc + Se), device=dev)
+    outs = torch.empty_like(ref_outs)
+    lses = torch.empty_like(ref_lses)
+    nb = max(pkv.decode_workspace_bytes(B, Hq, Sc * T, T, D, 0, S),
+             pkv.decode_workspace_bytes(B, Hq, Se * Te, Te, D, 0, Se_))
+    ws = torch.zeros(max(16, nb) // 4 + 4, device=dev)
+    merge_stream = torch.cuda.Stream()
+    decoded = [torch.cuda.Event() for _ in range(L)]
+    merged = torch.cuda.Event()
+
+    def step(evs=None):
+        for layer in range(L):
+            if evs is not None:
+                evs[layer][0].record(stream)
+            pkv.decode_attention(cpool, layer, qs[layer], dct, dcc, 0, Sc * T, T, w.scale,
+                                 po[layer], pl[layer], workspace=ws, split_tokens=S, stream=stream)
+            if evs is not None:
+                evs[layer][1].record(stream)
+            pkv.decode_attention(pool, layer, qs[layer], det, dec, 0, Se * Te, Te, w.scale,
+                                 po[layer], pl[layer], workspace=ws, split_tokens=Se_,
+                                 slot_offset=Sc, stream=stream)
+            decoded[layer].record(stream)
+            merge_stream.wait_event(decoded[layer])
+            pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=merge_stream)
+        merged.record(merge_stream)
+        stream.wait_event(merged)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(K):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L)] for _ in range(K)]
+    for k in range(K):
+        step(ev[k])
+    torch.cuda.synchronize()
+    comp_ms = float(np.mean([a.elapsed_time(b) for evk in ev for (a, b) in evk]))
+    # the cost of the representation, against the exact path's own result
+    d_out = float((outs - ref_outs).abs().max())
+    d_lse = float((lses - ref_lses).abs().max())
+
+    comp_bytes_layer = int(c.sum()) * 2 * Hkv * D + int(npc.sum()) * 2 * Hkv * 4
+    exact_bytes_layer = int(ectx.sum()) * 2 * Hkv * D * 2
+    moved = (comp_bytes_layer + exact_bytes_layer) * L
+    kv = w.kv_bytes_per_step
+    return {
+        "metric": "decode attention KV GB/s (% of HBM peak) and tokens/s at 262K ctx, 1 GPU",
+        "value": round(kv / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "value_kind": "exact-history bytes served per second (compact pages move fewer)",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: pages older than the newest {cl['exact_tail']} tokens "
+                               f"served from compact E4M3 pages (per-block FP32 scale), the tail "
+                               f"exact; compact run tile {T} split {S}, exact run tile {Te} "
+                               f"split {Se_}", "compact_tokens": int(c.sum()),
+                   "exact_tokens": int(ectx.sum())},
+        "tokens_per_s": round(B / (ms * 1e-3), 2),
+        "bytes_moved_per_step": moved,
+        "bytes_per_token_layer": {"exact": 2 * Hkv * D * 2,
+                                  "compact": round(comp_bytes_layer / max(1, int(c.sum())), 3)},
+        "vs_exact_path": {"max_abs_out": d_out, "max_abs_lse": d_lse},
+        "convert": {"pages": P, "ms": round(convert_ms, 3),
+                    "GBs_read": round(P * pool.page_bytes / (convert_ms * 1e-3) / 1e9, 1),
+                    "crc_recomputed_equal": crc_ok},
+        "roofline": {"bound": "hbm", "kernel": "decode_fp8_kernel",
+                     "achieved": round(comp_bytes_layer / (comp_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(comp_bytes_layer / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": comp_bytes_layer,
+                     "avg_launch_ms": round(comp_ms, 5), "traffic": None},
     }
 
 

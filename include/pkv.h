@@ -82,7 +82,7 @@ typedef struct pkv_pool pkv_pool;   /* opaque host-side handle */
 const char* pkv_last_error(void);
 
 /* Library ABI version (PKV_ABI_VERSION). */
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 int32_t pkv_abi_version(void);
 
 /* Bytes of one physical page (all layers) for `geom`. */
@@ -105,6 +105,63 @@ int pkv_pool_create(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes,
 int pkv_pool_info(const pkv_pool* pool, int64_t* num_pages, uint64_t* page_bytes,
                   void** dev_arena);
 int pkv_pool_destroy(pkv_pool* pool);
+
+/* --------------------------------------------------------- compact pool --
+ * Older pages kept in a compact representation (KV-cache engineering page,
+ * section "Exact recent pages, compact older pages": a request's history is
+ * served as runs of two representations; a page is converted once it is
+ * fully written in every layer, its CRC computed and the page published;
+ * until then it is served exact).  The pages name no format; here:
+ *   codes   E4M3 (OCP 8-bit float: sign, 4 exponent bits with bias 7,
+ *           3 mantissa bits, largest finite 448), one byte per element;
+ *   scale   one FP32 per (layer, page, K|V, kv head) block:
+ *           amax / 448 in FP32 (1 for an all-zero block);
+ *   code    E4M3 rounding of the FP32 quotient x / scale: to nearest, ties
+ *           to even, saturating at 448, the input's sign kept; the element
+ *           stands for value(code) * scale.  Inputs must be finite.
+ * Arena layout: codes [layer][page][K|V][kv_head][16,384-byte block], then
+ * scales [layer][page][K|V][kv_head] FP32.  A block holds 64 tokens x 256
+ * channels as 1,024 pieces of 16 bytes in the compact kernel's load order:
+ *   K piece ((h*2 + t)*4 + kk)*64 + q*16 + r: token 32h + 8(r/4) + 4t + r%4,
+ *     bytes 0..7 channels 64kk + 8q .. +7, bytes 8..15 channels
+ *     64kk + 32 + 8q .. +7;
+ *   V piece (d/16)*64 + q*16 + d%16: channel d, bytes 0..7 tokens
+ *     8q .. 8q+7, bytes 8..15 tokens 32 + 8q .. +7.
+ * A compact page (all layers) is pkv_compact_page_bytes = num_layers x
+ * 2 x num_kv_heads x (16,384 + 4) bytes: half an exact page plus scales.
+ * A compact pool is created like an exact one (explicit size, whole pages)
+ * and is accepted by pkv_page_table_validate/write and pkv_decode_attention
+ * (default or MFMA kernel), which then reads codes and scales; it is refused
+ * by pkv_append_kv and the stager (compact pages are immutable).
+ * pkv_pool_format reports PKV_FORMAT_BF16 or PKV_FORMAT_E4M3. */
+enum { PKV_FORMAT_BF16 = 0, PKV_FORMAT_E4M3 = 1 };
+int pkv_compact_page_bytes(const pkv_geom* geom, uint64_t* page_bytes_out);
+int pkv_compact_pool_create(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes,
+                            pkv_pool** pool_out);
+int pkv_pool_format(const pkv_pool* pool, int32_t* format_out);
+
+/* Convert whole exact pages into compact pages and publish their CRC.
+ * For i < n: exact page dev_src_pages[i] of `exact` (every layer, K and V,
+ * every kv head) is written as compact page dev_dst_pages[i] of `compact`,
+ * then dev_crc[i] receives the CRC-32 of that compact page.  Both pools must
+ * have the same geometry.  dev_src_pages, dev_dst_pages: device int32 [n];
+ * dev_crc: device uint32 [n].  An id outside its pool is skipped (nothing is
+ * written, its CRC is 0); two entries naming one destination race.  The
+ * caller converts only pages fully written in every layer and keeps serving
+ * them exact until it has the CRC and switches its tables (publishes).
+ * Queued on `stream` (two launches), no host wait; on a stream of its own it
+ * runs beside decode, which never waits for it.
+ *
+ * CRC-32 here is the reflected 0x04C11DB7 code with initial value and final
+ * xor 0xFFFFFFFF, over the compact page's bytes: for each layer in order,
+ * its code blocks (2 x num_kv_heads x 16,384 bytes as stored), then its
+ * scales (2 x num_kv_heads FP32, little endian).  pkv_compact_crc recomputes
+ * it for compact pages already written (to verify a page before use). */
+int pkv_compact_convert(const pkv_pool* exact, const pkv_pool* compact,
+                        const int32_t* dev_src_pages, const int32_t* dev_dst_pages, int32_t n,
+                        uint32_t* dev_crc, void* stream);
+int pkv_compact_crc(const pkv_pool* compact, const int32_t* dev_pages, int32_t n,
+                    uint32_t* dev_crc, void* stream);
 
 /* ---------------------------------------------------------- page table --
  * A page table is int32 [batch][pt_stride] in row-major order: entry i of
@@ -135,7 +192,9 @@ int pkv_page_table_write(const pkv_pool* pool, const int32_t* host_table,
  * request b covers tokens [t T, min((t+1) T, ctx_b)).  One call covers the
  * token window [token_begin, token_begin + token_count); both are
  * multiples of tile_tokens, and the window writes slots
- * [token_begin / T, (token_begin + token_count) / T) of every row.  A tile
+ * [token_begin / T, (token_begin + token_count) / T) of every row, each
+ * shifted by opts.slot_offset.  With a compact pool the keys and values are
+ * the compact pages' dequantised elements.  A tile
  * with no token of the request (ctx_b <= t T) is written as out = 0,
  * lse = -inf.  One call over the whole history (token_begin = 0) and
  * several calls over consecutive windows (staged tiles) write bit-identical
@@ -166,6 +225,10 @@ typedef struct pkv_decode_opts {
                             tile_tokens.  The split is a pure function of these options and
                             tile_tokens, never of batch, lengths or the device, so staged and
                             resident calls with the same options agree bit for bit. */
+  int32_t slot_offset;   /* 0 default; added to every slot the call writes, so the runs of
+                            two representations (a compact older run and an exact recent
+                            run, each with its own table) fill disjoint slots of one
+                            partial buffer for a single merge. */
 } pkv_decode_opts;
 
 int pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,

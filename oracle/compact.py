@@ -62,21 +62,16 @@ def e4m3_encode(y):
     """FP32 values -> E4M3 codes: the nearest finite value, ties to the even
     code (mantissa bit 0), magnitudes past 448 saturate to 448; the code's
     sign is the input's sign bit (so -0.0 and negatives that round to zero
-    give 0x80)."""
+    give 0x80).
+
+    Saturation is a clamp to +-448 (exact; it keeps the sign of zero); the
+    rounding is torch's float8_e4m3fn conversion, a library routine for
+    exactly this round-to-nearest-even (pinned against the format's value
+    table by brute force in the tests)."""
+    import torch
     y = np.asarray(y, dtype=np.float32)
-    a = np.abs(y.astype(np.float64)).ravel()
-    neg = np.signbit(y).ravel()
-    idx = np.searchsorted(_POS, a)                  # first value >= a
-    idx = np.clip(idx, 0, 126)
-    lo = np.clip(idx - 1, 0, 126)
-    d_hi = np.abs(_POS[idx] - a)
-    d_lo = np.abs(a - _POS[lo])
-    pick = np.where(d_lo < d_hi, lo, idx)
-    tie = (d_lo == d_hi) & (lo != idx)
-    pick = np.where(tie, np.where(lo % 2 == 0, lo, idx), pick)
-    pick = np.where(a >= _POS[126], 126, pick)      # saturate
-    code = pick.astype(np.uint8) | np.where(neg, 0x80, 0).astype(np.uint8)
-    return code.reshape(y.shape)
+    t = torch.from_numpy(np.ascontiguousarray(y)).clamp(-E4M3_MAX, E4M3_MAX)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy().reshape(y.shape)
 
 
 def e4m3_decode(codes):
@@ -109,26 +104,35 @@ def dequantize(codes, scale):
 
 def quantize_history(x, page_tokens=64):
     """A history [tokens, D] (float32 values) cut into blocks of page_tokens
-    rows, each quantised with its own scale; a trailing partial block is
-    quantised over the rows it has.  Returns (codes [tokens, D], scales
-    [n_blocks] float32)."""
+    rows, each quantised with its own scale (quantize_block, applied to all
+    blocks at once); a trailing partial block is quantised over the rows it
+    has.  Returns (codes [tokens, D], scales [n_blocks] float32)."""
     x = np.asarray(x, dtype=np.float32)
+    n, D = x.shape
+    full = n // page_tokens
     codes = np.empty(x.shape, dtype=np.uint8)
     scales = []
-    for b0 in range(0, x.shape[0], page_tokens):
-        c, s = quantize_block(x[b0:b0 + page_tokens])
-        codes[b0:b0 + page_tokens] = c
-        scales.append(s)
+    if full:
+        xb = x[:full * page_tokens].reshape(full, page_tokens, D)
+        amax = np.max(np.abs(xb), axis=(1, 2)).astype(np.float32)
+        s = np.where(amax == 0, np.float32(1.0),
+                     (amax / np.float32(E4M3_MAX)).astype(np.float32)).astype(np.float32)
+        y = (xb / s[:, None, None]).astype(np.float32)
+        codes[:full * page_tokens] = e4m3_encode(y).reshape(full * page_tokens, D)
+        scales.extend(s.tolist())
+    if n > full * page_tokens:
+        c, s1 = quantize_block(x[full * page_tokens:])
+        codes[full * page_tokens:] = c
+        scales.append(s1)
     return codes, np.array(scales, dtype=np.float32)
 
 
 def dequantize_history(codes, scales, page_tokens=64):
-    """Inverse of quantize_history's representation: float64 [tokens, D]."""
+    """Inverse of quantize_history's representation: float64 [tokens, D],
+    each element value(code) times its block's scale."""
     codes = np.asarray(codes, dtype=np.uint8)
-    out = np.empty(codes.shape, dtype=np.float64)
-    for i, b0 in enumerate(range(0, codes.shape[0], page_tokens)):
-        out[b0:b0 + page_tokens] = dequantize(codes[b0:b0 + page_tokens], scales[i])
-    return out
+    block = np.arange(codes.shape[0]) // page_tokens
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[block][:, None]
 
 
 def crc32(data):
@@ -138,17 +142,18 @@ def crc32(data):
 
 
 def lse_error_bound(q, k, k_hat, scale):
-    """Upper bound on |lse(q . k_hat) - lse(q . k)| for one query over one
-    set of keys: log-sum-exp moves by at most the largest change of any one
+    """Upper bound on |lse(q . k_hat) - lse(q . k)| for a query over one set
+    of keys: log-sum-exp moves by at most the largest change of any one
     score, and score j changes by scale * |q . (k_hat_j - k_j)|.
 
-    q [D], k and k_hat [n, D] (float64).  Returns a float.
-    """
+    q [D] or [H, D] (several queries over the same keys), k and k_hat
+    [n, D] (float64).  Returns a float, or an array [H]."""
     q = np.asarray(q, dtype=np.float64)
     dk = np.asarray(k_hat, dtype=np.float64) - np.asarray(k, dtype=np.float64)
     if dk.shape[0] == 0:
-        return 0.0
-    return float(np.max(np.abs(dk @ q)) * abs(scale))
+        return 0.0 if q.ndim == 1 else np.zeros(q.shape[0])
+    d = np.abs(dk @ q.T)                               # [n] or [n, H]
+    return (float(np.max(d)) if q.ndim == 1 else np.max(d, axis=0)) * abs(scale)
 
 
 def two_runs(x_bits, compact_tokens, page_tokens=64):

@@ -7,9 +7,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <vector>
 
+#include "compact.h"
 #include "kernels.h"
 #include "pool.h"
 
@@ -65,6 +67,37 @@ uint64_t page_layer_bytes(const pkv_geom* g) {
   return 2ull * (uint64_t)g->num_kv_heads * (uint64_t)g->page_tokens * (uint64_t)g->head_dim * 2ull;
 }
 
+// Compact (layer, page): codes of 2 x Hkv blocks, and their 2 x Hkv scales.
+uint64_t compact_code_bytes(const pkv_geom* g) {
+  return 2ull * (uint64_t)g->num_kv_heads * (uint64_t)pkv::kCompactBlockBytes;
+}
+uint64_t compact_scale_bytes(const pkv_geom* g) { return 2ull * (uint64_t)g->num_kv_heads * 4ull; }
+
+int create_pool(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes, int32_t format,
+                pkv_pool** pool_out);
+
+// CRC-32 arithmetic on the host (reflected representation: bit 31 is the
+// coefficient of x^0): a * b mod the polynomial, and x^(8 n).
+constexpr uint32_t kCrcPoly = 0xEDB88320u;
+uint32_t gf_mul(uint32_t a, uint32_t b) {
+  uint32_t p = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (a & (0x80000000u >> i)) p ^= b;
+    b = (b & 1u) ? (b >> 1) ^ kCrcPoly : (b >> 1);
+  }
+  return p;
+}
+uint32_t x_pow_bytes(uint64_t n) {       // x^(8 n) mod P by square and multiply
+  uint32_t result = 0x80000000u;          // x^0
+  uint32_t base = 0x00800000u;            // x^8
+  while (n) {
+    if (n & 1u) result = gf_mul(result, base);
+    base = gf_mul(base, base);
+    n >>= 1;
+  }
+  return result;
+}
+
 // Tokens per work-group for a tile length: the requested split, else the
 // largest multiple of 64 that divides tile_tokens and is <= kDefaultSplit.
 int split_for(int tile_tokens, const pkv_decode_opts* opts, int* split_out) {
@@ -116,10 +149,37 @@ PKV_API int pkv_page_bytes(const pkv_geom* geom, uint64_t* page_bytes_out) {
 
 PKV_API int pkv_pool_create(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes,
                             pkv_pool** pool_out) {
+  return create_pool(geom, dev_arena, arena_bytes, PKV_FORMAT_BF16, pool_out);
+}
+
+PKV_API int pkv_compact_pool_create(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes,
+                                    pkv_pool** pool_out) {
+  return create_pool(geom, dev_arena, arena_bytes, PKV_FORMAT_E4M3, pool_out);
+}
+
+PKV_API int pkv_compact_page_bytes(const pkv_geom* geom, uint64_t* page_bytes_out) {
+  if (int rc = check_geom(geom)) return rc;
+  if (!page_bytes_out) return fail(PKV_ERR_INVALID_ARG, "page_bytes_out is NULL");
+  *page_bytes_out = (compact_code_bytes(geom) + compact_scale_bytes(geom)) * (uint64_t)geom->num_layers;
+  return ok();
+}
+
+PKV_API int pkv_pool_format(const pkv_pool* pool, int32_t* format_out) {
+  if (!pool || !format_out) return fail(PKV_ERR_INVALID_ARG, "pool or format_out is NULL");
+  *format_out = pool->format;
+  return ok();
+}
+
+namespace {
+int create_pool(const pkv_geom* geom, void* dev_arena, uint64_t arena_bytes, int32_t format,
+                pkv_pool** pool_out) {
   if (int rc = check_geom(geom)) return rc;
   if (!pool_out) return fail(PKV_ERR_INVALID_ARG, "pool_out is NULL");
   *pool_out = nullptr;
-  const uint64_t pb = page_layer_bytes(geom) * (uint64_t)geom->num_layers;
+  const bool compact = format == PKV_FORMAT_E4M3;
+  const uint64_t plb = compact ? compact_code_bytes(geom) : page_layer_bytes(geom);
+  const uint64_t pb =
+      (compact ? plb + compact_scale_bytes(geom) : plb) * (uint64_t)geom->num_layers;
   if (arena_bytes == 0)
     return fail(PKV_ERR_AUTO_SIZE_REFUSED,
                 "arena_bytes = 0: an automatic pool size is refused; pass an explicit size, a "
@@ -146,11 +206,14 @@ PKV_API int pkv_pool_create(const pkv_geom* geom, void* dev_arena, uint64_t aren
   p->base = dev_arena;
   p->bytes = arena_bytes;
   p->page_bytes = pb;
-  p->page_layer_bytes = page_layer_bytes(geom);
+  p->page_layer_bytes = plb;
   p->num_pages = (int64_t)pages;
+  p->format = format;
+  p->scale_offset = compact ? plb * (uint64_t)geom->num_layers * pages : 0;
   *pool_out = p;
   return ok();
 }
+}  // namespace
 
 PKV_API int pkv_pool_info(const pkv_pool* pool, int64_t* num_pages, uint64_t* page_bytes,
                           void** dev_arena) {
@@ -286,7 +349,13 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
     return fail(PKV_ERR_INVALID_ARG,
                 "pt_stride = %d covers %lld tokens, less than token_count = %d", pt_stride,
                 (long long)pt_stride * G.page_tokens, token_count);
-  const int first_slot = token_begin / tile_tokens;
+  const int slot_offset = opts ? opts->slot_offset : 0;
+  if (slot_offset < 0) return fail(PKV_ERR_INVALID_ARG, "opts.slot_offset = %d is negative", slot_offset);
+  if (pool->format == PKV_FORMAT_E4M3 && kernel != 2)
+    return fail(PKV_ERR_INVALID_ARG, "a compact pool is read by the MFMA kernel only (opts.kernel 0 or 2)");
+  const int64_t first_slot64 = (int64_t)slot_offset + token_begin / tile_tokens;
+  if (first_slot64 > 65535) return fail(PKV_ERR_INVALID_ARG, "first slot %lld exceeds 65535", (long long)first_slot64);
+  const int first_slot = (int)first_slot64;
   const int n_tiles = token_count / tile_tokens;
   if (num_slots < 1 || (int64_t)first_slot + n_tiles > num_slots)
     return fail(PKV_ERR_INVALID_ARG, "slots %d..%d of this window exceed num_slots = %d",
@@ -344,8 +413,34 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
     a.out_slots = n_split;
     a.out_slot0 = 0;
   }
-  hipError_t e = (kernel == 1) ? pkv::launch_decode_valu(a, batch, group, s)
-                               : pkv::launch_decode_mfma(a, batch, group, s);
+  hipError_t e;
+  if (pool->format == PKV_FORMAT_E4M3) {
+    pkv::CompactDecodeArgs c;
+    c.codes = static_cast<const uint8_t*>(pool->base);
+    c.scales = reinterpret_cast<const float*>(static_cast<const char*>(pool->base) + pool->scale_offset);
+    c.page_bytes = (int64_t)pool->page_layer_bytes;
+    c.layer_off = (int64_t)pool->page_layer_bytes * pool->num_pages * layer;
+    c.scale_layer_off = (int64_t)2 * G.num_kv_heads * pool->num_pages * layer;
+    c.num_pages = a.num_pages;
+    c.num_kv_heads = a.num_kv_heads;
+    c.q = a.q;
+    c.table = a.table;
+    c.pt_stride = a.pt_stride;
+    c.ctx_lens = a.ctx_lens;
+    c.num_q_heads = a.num_q_heads;
+    c.token_begin = a.token_begin;
+    c.token_count = a.token_count;
+    c.split_tokens = a.split_tokens;
+    c.scale_log2 = a.scale_log2;
+    c.out_o = a.out_o;
+    c.out_lse = a.out_lse;
+    c.out_slots = a.out_slots;
+    c.out_slot0 = a.out_slot0;
+    e = pkv::launch_decode_fp8(c, batch, group, s);
+  } else {
+    e = (kernel == 1) ? pkv::launch_decode_valu(a, batch, group, s)
+                      : pkv::launch_decode_mfma(a, batch, group, s);
+  }
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
   if (split != tile_tokens) {
     pkv::MergeArgs m;
@@ -396,6 +491,8 @@ PKV_API int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* de
                           int32_t pt_stride, const int32_t* dev_positions, int32_t batch,
                           const void* k_new, const void* v_new, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (pool->format != PKV_FORMAT_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "compact pages are immutable: append to the exact pool");
   const pkv_geom& G = pool->geom;
   if (layer < 0 || layer >= G.num_layers)
     return fail(PKV_ERR_INVALID_ARG, "layer = %d outside 0..%d", layer, G.num_layers - 1);
@@ -419,5 +516,76 @@ PKV_API int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* de
   a.v = static_cast<const uint16_t*>(v_new);
   hipError_t e = pkv::launch_append(a, batch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "append launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+PKV_API int pkv_compact_convert(const pkv_pool* exact, const pkv_pool* compact,
+                                const int32_t* dev_src_pages, const int32_t* dev_dst_pages,
+                                int32_t n, uint32_t* dev_crc, void* stream) {
+  if (!exact || !compact) return fail(PKV_ERR_INVALID_ARG, "exact or compact pool is NULL");
+  if (exact->format != PKV_FORMAT_BF16 || compact->format != PKV_FORMAT_E4M3)
+    return fail(PKV_ERR_INVALID_ARG, "convert takes an exact (bf16) pool and a compact (E4M3) pool");
+  const pkv_geom& a = exact->geom;
+  const pkv_geom& b = compact->geom;
+  if (a.num_layers != b.num_layers || a.num_kv_heads != b.num_kv_heads ||
+      a.head_dim != b.head_dim || a.page_tokens != b.page_tokens)
+    return fail(PKV_ERR_GEOMETRY, "the two pools differ in geometry");
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n = %d is negative", n);
+  if (n == 0) return ok();
+  if (!dev_src_pages || !dev_dst_pages || !dev_crc)
+    return fail(PKV_ERR_INVALID_ARG, "dev_src_pages, dev_dst_pages or dev_crc is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < n; i0 += 65535) {          // grid z is at most 65535
+    const int32_t m = std::min<int32_t>(65535, n - i0);
+    pkv::ConvertArgs c;
+    c.src = static_cast<const uint16_t*>(exact->base);
+    c.src_page_elems = (int64_t)(exact->page_layer_bytes / 2);
+    c.src_num_pages = exact->num_pages;
+    c.codes = static_cast<uint8_t*>(compact->base);
+    c.scales = reinterpret_cast<float*>(static_cast<char*>(compact->base) + compact->scale_offset);
+    c.dst_page_bytes = (int64_t)compact->page_layer_bytes;
+    c.dst_num_pages = compact->num_pages;
+    c.num_layers = a.num_layers;
+    c.num_kv_heads = a.num_kv_heads;
+    c.src_pages = dev_src_pages + i0;
+    c.dst_pages = dev_dst_pages + i0;
+    c.n = m;
+    hipError_t e = pkv::launch_convert(c, s);
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "convert launch failed: %s", hipGetErrorString(e));
+  }
+  return pkv_compact_crc(compact, dev_dst_pages, n, dev_crc, stream);
+}
+
+PKV_API int pkv_compact_crc(const pkv_pool* compact, const int32_t* dev_pages, int32_t n,
+                            uint32_t* dev_crc, void* stream) {
+  if (!compact) return fail(PKV_ERR_INVALID_ARG, "compact pool is NULL");
+  if (compact->format != PKV_FORMAT_E4M3) return fail(PKV_ERR_INVALID_ARG, "not a compact pool");
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n = %d is negative", n);
+  if (n == 0) return ok();
+  if (!dev_pages || !dev_crc) return fail(PKV_ERR_INVALID_ARG, "dev_pages or dev_crc is NULL");
+  const pkv_geom& G = compact->geom;
+  pkv::CrcArgs c;
+  c.codes = static_cast<const uint8_t*>(compact->base);
+  c.scales = reinterpret_cast<const float*>(static_cast<const char*>(compact->base) +
+                                            compact->scale_offset);
+  c.page_bytes = (int64_t)compact->page_layer_bytes;
+  c.num_pages = compact->num_pages;
+  c.num_layers = G.num_layers;
+  c.scale_count = 2 * G.num_kv_heads;
+  const uint64_t seg = compact->page_layer_bytes / 256;
+  for (int k = 0; k < 8; ++k) c.x_seg[k] = x_pow_bytes(seg << k);
+  const uint64_t sb = 4ull * (uint64_t)c.scale_count;
+  c.x_scales = x_pow_bytes(sb);
+  c.x_layer = x_pow_bytes(compact->page_layer_bytes + sb);
+  c.init_term = gf_mul(0xFFFFFFFFu, x_pow_bytes((compact->page_layer_bytes + sb) * G.num_layers));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < n; i0 += 1 << 20) {
+    const int32_t m = std::min<int32_t>(1 << 20, n - i0);
+    c.pages = dev_pages + i0;
+    c.crc = dev_crc + i0;
+    c.n = m;
+    hipError_t e = pkv::launch_crc(c, s);
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "crc launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }

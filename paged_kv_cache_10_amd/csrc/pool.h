@@ -12,6 +12,8 @@ struct pkv_pool {
   uint64_t page_bytes;        // one physical page, all layers
   uint64_t page_layer_bytes;  // one (layer, page)
   int64_t num_pages;
+  int32_t format;             // PKV_FORMAT_BF16 or PKV_FORMAT_E4M3
+  uint64_t scale_offset;      // E4M3: byte offset of the scale region in the arena
 };
 
 namespace pkv {

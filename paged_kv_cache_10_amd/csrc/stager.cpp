@@ -79,6 +79,8 @@ PKV_API int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_
   if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!staging) return fail(PKV_ERR_INVALID_ARG, "staging pool is NULL");
+  if (staging->format != PKV_FORMAT_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "the staging pool must hold exact (bf16) pages");
   if (!host_arena || !dev_tables) return fail(PKV_ERR_INVALID_ARG, "host_arena or dev_tables is NULL");
   if (host_layers < 1) return fail(PKV_ERR_INVALID_ARG, "host_layers must be >= 1");
   const uint64_t plb = staging->page_layer_bytes;

@@ -357,6 +357,57 @@ def device_scatter(pool, w, layer, b, table_row, k, v, pad_value=0):
 
 
 # ----------------------------------------------------------------------------
+# compact (one byte per element) block layout: where each (token, channel)
+# code of a 64 x 256 block sits among the block's 16,384 bytes
+
+
+def _kc_byte_map():
+    """[64 tokens, 256 channels] -> byte offset in a compact K block."""
+    out = np.empty((64, 256), dtype=np.int64)
+    for ld in range(16):                        # load index (h*2 + t)*4 + kk
+        h, t, kk = ld // 8, (ld // 4) % 2, ld % 4
+        for lane in range(64):
+            q, r = lane // 16, lane % 16
+            j = 32 * h + 8 * (r // 4) + 4 * t + r % 4
+            piece = ld * 64 + lane
+            for e in range(8):
+                out[j, 64 * kk + 8 * q + e] = piece * 16 + e
+                out[j, 64 * kk + 32 + 8 * q + e] = piece * 16 + 8 + e
+    return out
+
+
+def _vc_byte_map():
+    """[64 tokens, 256 channels] -> byte offset in a compact V block."""
+    out = np.empty((64, 256), dtype=np.int64)
+    for db in range(16):
+        for lane in range(64):
+            q, d = lane // 16, 16 * db + lane % 16
+            piece = db * 64 + lane
+            for e in range(8):
+                out[8 * q + e, d] = piece * 16 + e
+                out[32 + 8 * q + e, d] = piece * 16 + 8 + e
+    return out
+
+
+KC_BYTES = _kc_byte_map()
+VC_BYTES = _vc_byte_map()
+
+
+def compact_block_image(codes, kind):
+    """Codes [64, 256] (token, channel) -> the block's 16,384 bytes."""
+    m = KC_BYTES if kind == "k" else VC_BYTES
+    img = np.zeros(64 * 256, dtype=np.uint8)
+    img[m] = codes
+    return img
+
+
+def compact_block_codes(image, kind):
+    """The block's 16,384 bytes -> codes [64, 256] (token, channel)."""
+    m = KC_BYTES if kind == "k" else VC_BYTES
+    return np.asarray(image, dtype=np.uint8)[m]
+
+
+# ----------------------------------------------------------------------------
 # merge stress draws
 
 

@@ -30,6 +30,8 @@ EXPORTS = [
     "pkv_stager_retire", "pkv_stager_info", "pkv_stager_fail", "pkv_stager_destroy",
     "pkv_admit_create", "pkv_admit_add", "pkv_admit_set_target", "pkv_admit_remove",
     "pkv_admit_step", "pkv_admit_get_counts", "pkv_admit_events", "pkv_admit_destroy",
+    "pkv_compact_page_bytes", "pkv_compact_pool_create", "pkv_pool_format",
+    "pkv_compact_convert", "pkv_compact_crc",
 ]
 
 
@@ -46,7 +48,8 @@ class Geom(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32)]
+    _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("slot_offset", ctypes.c_int32)]
 
 
 class AdmitCounts(ctypes.Structure):
@@ -96,6 +99,11 @@ def lib():
         L.pkv_pool_info.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(U64),
                                     ctypes.POINTER(P)]
         L.pkv_pool_destroy.argtypes = [P]
+        L.pkv_compact_page_bytes.argtypes = [ctypes.POINTER(Geom), ctypes.POINTER(U64)]
+        L.pkv_compact_pool_create.argtypes = [ctypes.POINTER(Geom), P, U64, ctypes.POINTER(P)]
+        L.pkv_pool_format.argtypes = [P, I32P]
+        L.pkv_compact_convert.argtypes = [P, P, P, P, I32, P, P]
+        L.pkv_compact_crc.argtypes = [P, P, I32, P, P]
         L.pkv_page_table_validate.argtypes = [P, I32P, I32P, I32, I32]
         L.pkv_page_table_write.argtypes = [P, I32P, I32P, I32, I32, P, P, P]
         L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32,
@@ -159,12 +167,12 @@ def _i32_array(a):
     return a, a.ctypes.data_as(I32P)
 
 
-def _opts(kernel, split_tokens):
+def _opts(kernel, split_tokens, slot_offset=0):
     if kernel in (0, 0.0, None):
         k = 0
     else:
         k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    return DecodeOpts(k, int(split_tokens or 0))
+    return DecodeOpts(k, int(split_tokens or 0), int(slot_offset or 0))
 
 
 def abi_version():
@@ -180,16 +188,19 @@ def page_bytes(num_layers, num_kv_heads, head_dim=256, page_tokens=64):
 
 class Pool:
     """A page pool over a caller-owned arena (any device tensor; its bytes are
-    the arena).  `arena_bytes` defaults to the tensor's size; 0 is refused."""
+    the arena).  `arena_bytes` defaults to the tensor's size; 0 is refused.
+    compact=True makes a pool of compact (E4M3) pages."""
 
     def __init__(self, arena, num_layers, num_kv_heads, head_dim=256, page_tokens=64,
-                 arena_bytes=None):
+                 arena_bytes=None, compact=False):
         self.arena = arena                     # keeps the memory alive
         self.geom = Geom(num_layers, num_kv_heads, head_dim, page_tokens)
         nbytes = arena.numel() * arena.element_size() if arena_bytes is None else int(arena_bytes)
         h = P()
         ptr = arena.data_ptr()
-        _check(lib().pkv_pool_create(ctypes.byref(self.geom), ptr, nbytes, ctypes.byref(h)))
+        create = lib().pkv_compact_pool_create if compact else lib().pkv_pool_create
+        _check(create(ctypes.byref(self.geom), ptr, nbytes, ctypes.byref(h)))
+        self.compact = compact
         self.handle = h
         n = ctypes.c_int64()
         pb = U64()
@@ -246,7 +257,7 @@ def decode_workspace_bytes(batch, num_q_heads, token_count, tile_tokens, head_di
 
 def decode_attention(pool, layer, q, dev_table, dev_ctx_lens, token_begin, token_count,
                      tile_tokens, scale, part_out, part_lse, workspace=None, kernel=0,
-                     split_tokens=0, stream=None):
+                     split_tokens=0, stream=None, slot_offset=0):
     """Tile partials of one layer for tokens [token_begin, token_begin + token_count).
 
     q: bf16 [B, Hq, D]; dev_table: int32 [B, pt_stride] (entry i = logical page
@@ -263,7 +274,7 @@ def decode_attention(pool, layer, q, dev_table, dev_ctx_lens, token_begin, token
         raise ValueError("dev_table must be [B, pt_stride]")
     if dev_table.stride(1) != 1:
         raise ValueError("dev_table rows must be contiguous")
-    o = _opts(kernel, split_tokens)
+    o = _opts(kernel, split_tokens, slot_offset)
     ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pkv_decode_attention(
@@ -430,3 +441,40 @@ class Admission:
             self.close()
         except Exception:
             pass
+
+
+def pool_format(pool):
+    f = I32()
+    _check(lib().pkv_pool_format(pool.handle, ctypes.byref(f)))
+    return {0: "bf16", 1: "e4m3"}[f.value]
+
+
+def compact_page_bytes(num_layers, num_kv_heads, head_dim=256, page_tokens=64):
+    g = Geom(num_layers, num_kv_heads, head_dim, page_tokens)
+    out = U64()
+    _check(lib().pkv_compact_page_bytes(ctypes.byref(g), ctypes.byref(out)))
+    return out.value
+
+
+def compact_convert(exact, compact, src_pages, dst_pages, crc, stream=None):
+    """Convert exact pages src_pages[i] into compact pages dst_pages[i] and
+    write each compact page's CRC-32 into crc[i].  src_pages, dst_pages:
+    device int32 [n]; crc: device int32 [n] (the CRC's 32 bits)."""
+    import torch
+    n = src_pages.numel()
+    if dst_pages.numel() != n or crc.numel() != n:
+        raise ValueError("src_pages, dst_pages and crc must have the same length")
+    _check(lib().pkv_compact_convert(
+        exact.handle, compact.handle, _ptr(src_pages, torch.int32, "src_pages"),
+        _ptr(dst_pages, torch.int32, "dst_pages"), n, _ptr(crc, torch.int32, "crc"),
+        _stream(stream)))
+
+
+def compact_crc(compact, pages, crc, stream=None):
+    """CRC-32 of compact pages already written: crc[i] for pages[i]."""
+    import torch
+    n = pages.numel()
+    if crc.numel() != n:
+        raise ValueError("pages and crc must have the same length")
+    _check(lib().pkv_compact_crc(compact.handle, _ptr(pages, torch.int32, "pages"), n,
+                                 _ptr(crc, torch.int32, "crc"), _stream(stream)))

@@ -213,3 +213,86 @@ def test_append_arguments_are_refused_on_the_host():
         rc, msg = call(**kw)
         assert rc == -1 and needle in msg, (kw, msg)
     assert call(batch=0)[0] == 0
+
+
+# ----------------------------------------------------------------------------
+# compact pages
+
+
+class FakeCompactPool(FakePool):
+    def __init__(self, pages, layers=16, hkv=4):
+        h = pkv.P()
+        g = geom(layers, hkv)
+        rc = pkv.lib().pkv_compact_pool_create(ctypes.byref(g), FAKE_ARENA,
+                                               pkv.compact_page_bytes(layers, hkv) * pages,
+                                               ctypes.byref(h))
+        assert rc == 0, err()
+        self.handle = h
+        n = ctypes.c_int64()
+        assert pkv.lib().pkv_pool_info(h, ctypes.byref(n), None, None) == 0
+        self.num_pages = n.value
+
+
+def test_compact_page_bytes_halve_the_exact_page():
+    # codes: one byte per element (half the bf16 page); scales: 2 x Hkv FP32 per layer
+    assert pkv.compact_page_bytes(16, 4) == 16 * (2 * 4 * 64 * 256 + 2 * 4 * 4)
+    assert pkv.compact_page_bytes(1, 4) * 2 - pkv.page_bytes(1, 4) == 2 * 2 * 4 * 4
+    L = pkv.lib()
+    h = pkv.P()
+    assert L.pkv_compact_pool_create(ctypes.byref(geom()), FAKE_ARENA, 0, ctypes.byref(h)) == -2
+    assert L.pkv_compact_pool_create(ctypes.byref(geom()), FAKE_ARENA,
+                                     pkv.compact_page_bytes(16, 4) * 3 + 1, ctypes.byref(h)) == -1
+    p = FakeCompactPool(10)
+    assert p.num_pages == 10
+    f = ctypes.c_int32()
+    assert L.pkv_pool_format(p.handle, ctypes.byref(f)) == 0 and f.value == 1
+    assert L.pkv_pool_format(FakePool(2).handle, ctypes.byref(f)) == 0 and f.value == 0
+
+
+def test_compact_pool_is_read_only_by_the_mfma_kernel():
+    rc, msg = decode_raw(FakeCompactPool(64), kernel=1)
+    assert rc == -1 and "compact" in msg
+    assert decode_raw(FakeCompactPool(64), batch=0)[0] == 0
+
+
+def test_slot_offset_is_checked():
+    L = pkv.lib()
+    pool = FakePool(64)
+    o = pkv.DecodeOpts(0, 0, -1)
+
+    def call(o, slots):
+        return L.pkv_decode_attention(pool.handle, 0, 1 << 20, 1 << 21, 64, 1 << 22, 1, 24, 0,
+                                      4096, 1024, 0.0625, 1 << 23, 1 << 24, slots, 1 << 25,
+                                      1 << 30, ctypes.byref(o), None), err()
+    rc, msg = call(pkv.DecodeOpts(0, 1024, -1), 8)
+    assert rc == -1 and "slot_offset" in msg
+    rc, msg = call(pkv.DecodeOpts(0, 1024, 5), 8)          # slots 5..8 of 8
+    assert rc == -1 and "num_slots" in msg
+
+
+def test_compact_pools_refuse_append_and_staging():
+    L = pkv.lib()
+    cp = FakeCompactPool(8)
+    assert L.pkv_append_kv(cp.handle, 0, 1 << 20, 4, 1 << 21, 2, 1 << 22, 1 << 23, None) == -1
+    assert "immutable" in err()
+    st = pkv.P()
+    rc = L.pkv_stager_create(cp.handle, 1 << 20, pkv.page_bytes(16, 4), 16, 1, 32768, 1,
+                             1 << 21, None, None, None, ctypes.byref(st))
+    assert rc == -1 and "exact" in err()
+
+
+def test_convert_and_crc_arguments_are_refused_on_the_host():
+    L = pkv.lib()
+    ex, cp = FakePool(8), FakeCompactPool(8)
+    args = (1 << 20, 1 << 21, 4, 1 << 22, None)
+    assert L.pkv_compact_convert(cp.handle, ex.handle, *args) == -1          # swapped formats
+    other = FakeCompactPool(8, layers=2)
+    assert L.pkv_compact_convert(ex.handle, other.handle, *args) == -3
+    assert "geometry" in err()
+    assert L.pkv_compact_convert(ex.handle, cp.handle, 1 << 20, 1 << 21, -1, 1 << 22, None) == -1
+    assert L.pkv_compact_convert(ex.handle, cp.handle, None, 1 << 21, 4, 1 << 22, None) == -1
+    assert L.pkv_compact_convert(ex.handle, cp.handle, None, None, 0, None, None) == 0   # nothing
+    assert L.pkv_compact_crc(ex.handle, 1 << 20, 4, 1 << 21, None) == -1
+    assert "compact" in err()
+    assert L.pkv_compact_crc(cp.handle, None, 4, 1 << 21, None) == -1
+    assert L.pkv_compact_crc(cp.handle, None, 0, None, None) == 0

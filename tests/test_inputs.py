@@ -154,3 +154,21 @@ def test_shorter_history_is_a_prefix():
         k2, v2 = I.draw_kv(w2, layer, 0)
         np.testing.assert_array_equal(k, k2[:, :70])
         np.testing.assert_array_equal(v, v2[:, :70])
+
+
+def test_compact_block_maps_are_bijections_with_the_stated_offsets():
+    for m in (I.KC_BYTES, I.VC_BYTES):
+        assert sorted(m.ravel().tolist()) == list(range(64 * 256))
+    # K: token 0 channels 0 / 32 share piece 0 (bytes 0 and 8); token 1 is
+    # row 1 of the same tile (piece 1); token 4 is tile 1 (load 4, piece 256)
+    assert I.KC_BYTES[0, 0] == 0 and I.KC_BYTES[0, 32] == 8 and I.KC_BYTES[0, 7] == 7
+    assert I.KC_BYTES[1, 0] == 16 and I.KC_BYTES[4, 0] == 256 * 16
+    assert I.KC_BYTES[0, 8] == 16 * 16 and I.KC_BYTES[0, 64] == 64 * 16
+    # V: channel d is row d%16 of block d/16; tokens 8q.. in bytes 0..7, the
+    # second half's tokens in bytes 8..15
+    assert I.VC_BYTES[0, 0] == 0 and I.VC_BYTES[32, 0] == 8 and I.VC_BYTES[8, 0] == 16 * 16
+    assert I.VC_BYTES[0, 1] == 16 and I.VC_BYTES[0, 16] == 64 * 16
+    r = np.random.default_rng(1)
+    c = r.integers(0, 256, (64, 256), dtype=np.uint8)
+    for kind in "kv":
+        np.testing.assert_array_equal(I.compact_block_codes(I.compact_block_image(c, kind), kind), c)

@@ -1,8 +1,9 @@
 """Pins for the compact-page oracle (CPU only): E4M3 codes, block scales,
 dequantisation, CRC-32 and the log-sum-exp error bound, each checked
 against something other than itself — the hand-derived fixture
-tests/golden/e4m3_codes.json, torch's float8_e4m3fn conversion, exact
-algebraic properties of the format and of CRC-32's catalogued constants —
+tests/golden/e4m3_codes.json, brute force over the format's value table,
+torch's float8_e4m3fn decoding, exact algebraic properties of the format and
+of CRC-32's catalogued constants —
 and planted mistakes that must each fail a pin."""
 
 import json
@@ -128,19 +129,32 @@ def pin_torch_decode(m):
     np.testing.assert_array_equal(m.decode(codes), ref)
 
 
-def pin_torch_encode(m):
-    """torch's float8_e4m3fn conversion rounds to nearest even; below its
-    overflow point (464) it agrees with the saturating definition."""
+def brute_encode(y):
+    """The definition by brute force over the value table: the nearest of
+    the 127 non-negative finite values to |y| (ties to the even code), past
+    448 the largest, with y's sign bit."""
+    y = np.asarray(y, dtype=np.float32).ravel()
+    vals = C.e4m3_values()[:127]
+    out = np.empty(y.size, dtype=np.uint8)
+    for i, v in enumerate(y.astype(np.float64)):
+        a = abs(v)
+        d = np.abs(vals - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+        out[i] = c | (0x80 if np.signbit(v) else 0)
+    return out
+
+
+def pin_brute_force_encode(m):
     r = np.random.default_rng(7)
     y = np.concatenate([
-        r.standard_normal(20000) * 10.0 ** r.uniform(-4, 2.6, 20000),
+        r.standard_normal(3000) * 10.0 ** r.uniform(-4, 3, 3000),
         # exact midpoints between neighbouring finite values (all ties)
         (C._POS[:-1] + C._POS[1:]) / 2.0,
         -(C._POS[:-1] + C._POS[1:]) / 2.0,
+        [0.0, -0.0, 448.0, 464.0, 470.0, -1e9, 2.0 ** -10, -(2.0 ** -10)],
     ]).astype(np.float32)
-    y = y[np.abs(y) < 464]
-    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    np.testing.assert_array_equal(m.encode(y), ref)
+    np.testing.assert_array_equal(m.encode(y), brute_encode(y))
 
 
 def pin_saturation(m):
@@ -187,7 +201,7 @@ def pin_crc(m):
 
 
 PINS = [pin_golden_decode, pin_golden_encode, pin_golden_block, pin_torch_decode,
-        pin_torch_encode, pin_saturation, pin_round_trip, pin_block_properties, pin_crc]
+        pin_brute_force_encode, pin_saturation, pin_round_trip, pin_block_properties, pin_crc]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -240,6 +254,12 @@ def test_lse_bound_holds_and_is_tight_for_one_key():
         assert abs(lse_hat - lse) <= b * (1 + 1e-9) + 1e-15
         if n == 1:
             assert abs(abs(lse_hat - lse) - b) <= 1e-12 * max(1.0, b)
+        # several queries at once give each query's own bound
+        qs = r.standard_normal((3, 256))
+        many = C.lse_error_bound(qs, k, k_hat, scale)
+        assert many.shape == (3,)
+        for i in range(3):
+            assert abs(many[i] - C.lse_error_bound(qs[i], k, k_hat, scale)) <= 1e-12
 
 
 def test_two_runs_splits_at_the_boundary():
