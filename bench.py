@@ -37,9 +37,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "9e90796fc0fc87d52fbaed851b6ca443f42c3de1fa88af8dd1a8ce32b1c5e986",
+    "source_sha256": "805167465b2b792b27851ddec9ae80e22d5abaa245b7be968c0d46d4b1b84b5a",
     "workload": "long262k", "tile": 4096, "split": 4096,
-    "fetch_kib": 524445.8, "fetch_scale": 1048576 / 524307.0,
+    "fetch_kib": 524445.7, "fetch_scale": 1048576 / 524317.7,
     "write_kib": 1584.1, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/device.h")
@@ -47,8 +47,8 @@ KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "91a8c714005fbaddffe646161a550cd92bf1d9e9d6f939fc696474eaeea7fa16",
-    "fetch_kib": 229798.0, "fetch_scale": 1048576 / 524303.75,
+    "source_sha256": "f20f502cc31174054d1de7161b0c8c4b7f3984a0190f1f950cc53756a0d1a4d2",
+    "fetch_kib": 229775.5, "fetch_scale": 1048576 / 524303.9,
     "write_kib": 1584.0, "write_scale": 1.0,
 }
 FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_amd/csrc/compact.h",
@@ -81,7 +81,7 @@ def pmc_traffic(workload, tile, split, kernel):
 # `overlap`: layer l's merge runs on a second stream while layer l+1 decodes.
 LAUNCH = {
     "long262k": dict(tile=4096, split=4096, overlap=True),   # 32K windows split-KV 8 ways
-    "conc": dict(tile=8192, split=2048, overlap=False),      # 8,192-token tiles per request
+    "conc": dict(tile=1984, split=1984, overlap=False),      # 16 full 1,984-token tiles per request
     "mixed": dict(tile=2048, split=2048, overlap=True),
     "tiny": dict(tile=1024, split=1024, overlap=False),
 }

@@ -10,8 +10,8 @@
 //          exact kernel keeps per 32-token chunk);
 //   QK     32 MFMAs (2 halves x 2 tiles x 8 k-steps); every E4M3 code is
 //          widened to bf16 exactly (an E4M3 value has at most 4 significant
-//          bits) right before its MFMA; the page's K scale multiplies the
-//          scores;
+//          bits), two per instruction, right before its MFMA; the page's K
+//          scale multiplies the scores;
 //   softmax base-2 running max and sum over the page's 64 scores;
 //   PV     64 MFMAs (2 halves x 16 channel blocks x hi/lo): P times the
 //          page's V scale, split p = hi + lo in bf16, so the product keeps
@@ -30,26 +30,21 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQPad = kHeadDim + 8;        // LDS row pitch of Q (bf16)
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Upper halves of two FP32 words as one bf16 pair (lo from x, hi from y).
-__device__ __forceinline__ uint32_t pack_hi(float x, float y) {
-  return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
-}
-
-// Eight E4M3 codes (bytes 0..7 of w0, w1) widened to eight bf16, exactly.
+// Eight E4M3 codes (bytes 0..7 of w0, w1) widened to eight bf16, exactly
+// (scale 1: v_cvt_scalef32_pk_bf16_fp8 converts two codes per instruction).
 __device__ __forceinline__ bf16x8_t widen8(uint32_t w0, uint32_t w1) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
-  const uint4 u = make_uint4(pack_hi(a[0], a[1]), pack_hi(b[0], b[1]), pack_hi(c[0], c[1]),
-                             pack_hi(d[0], d[1]));
-  return __builtin_bit_cast(bf16x8_t, u);
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  bf16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
 }
 
 // Keep the first `live` (0..8) bytes of a two-word group, zero the rest.
@@ -204,22 +199,6 @@ void decode_fp8_kernel(CompactDecodeArgs a) {
     return;
   }
 
-  for (int i = tid; i < 16 * (D / 8); i += kThreads) {
-    const int h = i / (D / 8);
-    const int c8 = i % (D / 8);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < G) v = reinterpret_cast<const uint4*>(a.q + (row0 + h) * D)[c8];
-    *reinterpret_cast<uint4*>(&q_lds[h * kQPad + 8 * c8]) = v;
-  }
-  __syncthreads();
-  const uint16_t* qrow = &q_lds[n * kQPad + 8 * q];
-
-  float m = -INFINITY;
-  float lsum = 0.f;
-  f32x4_t acc[16];
-#pragma unroll
-  for (int db = 0; db < 16; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   const uint8_t* layer_base = a.codes + a.layer_off;
   const float* layer_scales = a.scales + a.scale_layer_off;
   const int32_t* trow = a.table + (int64_t)b * a.pt_stride;
@@ -227,9 +206,19 @@ void decode_fp8_kernel(CompactDecodeArgs a) {
   const int n_pages = (t1 - t0 + PT - 1) / PT;
   const int my_pages = (n_pages > w) ? (n_pages - w + kWaves - 1) / kWaves : 0;
 
-  // lane j holds the id and the two scales of the wave's page j (at most 64
-  // pages per wave: split_tokens <= 16384)
+  // Prologue: page ids, the query group, the pages' scales and the first
+  // page's loads are issued before anything waits.  Lane j holds the id and
+  // the two scales of the wave's page j (at most 64 pages per wave:
+  // split_tokens <= 16384).
   int my_id = (lane < my_pages) ? trow[first_page + w + kWaves * lane] : -1;
+  uint4 qv[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * kThreads;
+    const int h = i / (D / 8);
+    qv[r] = (h < G) ? reinterpret_cast<const uint4*>(a.q + (row0 + h) * D)[i % (D / 8)]
+                    : make_uint4(0, 0, 0, 0);
+  }
   const bool id_ok = my_id >= 0 && my_id < a.num_pages;
   float my_sk = 0.f, my_sv = 0.f;
   if (id_ok) {
@@ -251,12 +240,27 @@ void decode_fp8_kernel(CompactDecodeArgs a) {
     pg.v = page + (int64_t)(a.num_kv_heads + g) * kCompactBlockBytes;
     return pg;
   };
-
   uint4 kr[16], vr[16];
+  PageRef cur = page_at(0);
   if (my_pages > 0) {
-    PageRef cur = page_at(0);
     load_blk(kr, cur.k, lane);
     load_blk(vr, cur.v, lane);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * kThreads;
+    *reinterpret_cast<uint4*>(&q_lds[(i / (D / 8)) * kQPad + 8 * (i % (D / 8))]) = qv[r];
+  }
+  __syncthreads();
+  const uint16_t* qrow = &q_lds[n * kQPad + 8 * q];
+
+  float m = -INFINITY;
+  float lsum = 0.f;
+  f32x4_t acc[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (my_pages > 0) {
     for (int j = 0; j + 1 < my_pages; ++j) {
       const PageRef nxt = page_at(j + 1);
       page_step<true>(kr, vr, acc, m, lsum, qrow, cur, a.scale_log2, q, lane, nxt);

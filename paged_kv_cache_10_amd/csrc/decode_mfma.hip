@@ -19,7 +19,8 @@
 //       16-byte load per lane.  P is split as p = hi + lo with hi, lo bf16
 //       (both round to nearest), two MFMAs per tile, so the product keeps
 //       ~2^-17 relative accuracy instead of bf16's 2^-9.
-// K/V loads of the next chunk are issued while the current chunk computes.
+// K/V loads of the next chunk are issued while the current chunk computes;
+// the first chunk's loads are in flight while the query group is staged.
 //
 // Padding (tokens at or past the length, or pages whose id is out of range)
 // scores -inf and its V values are zeroed before the MFMA, so NaN padding
@@ -157,11 +158,7 @@ __device__ __forceinline__ void chunk(uint4 (&kr)[2][8], uint4 (&vr)[16], f32x4_
   __builtin_amdgcn_sched_barrier(0);
 }
 
-#ifndef PKV_MFMA_RING
-#define PKV_MFMA_RING 1
-#endif
-
-template <int G, int kRing>
+template <int G>
 __global__ __launch_bounds__(kThreads)
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
@@ -198,13 +195,51 @@ void decode_mfma_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---- stage the query group (zero rows past G)
-  for (int i = tid; i < 16 * (D / 8); i += kThreads) {
+  const uint16_t* layer_base = a.arena + a.layer_off;
+  const int32_t* trow = a.table + (int64_t)b * a.pt_stride;
+  const int first_page = (t0 - a.token_begin) / PT;
+  const int n_pages = (t1 - t0 + PT - 1) / PT;
+  // this wave's pages: w, w + 4, ...
+  const int my_pages = (n_pages > w) ? (n_pages - w + kWaves - 1) / kWaves : 0;
+
+  // Prologue: the page ids, the query group and the first chunk's K/V loads
+  // are all issued before anything waits, so their latencies overlap.
+  // Page ids of this wave's pages (at most 64: split_tokens <= 16384): lane j
+  // holds the id of the wave's page j, read with readlane, so no dependent
+  // global load sits in front of K/V loads inside the loop.
+  const int my_id = (lane < my_pages) ? trow[first_page + w + kWaves * lane] : 0;
+  // the query group: 16 rows (zero past G) x 32 pieces = 2 pieces per thread
+  uint4 qv[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * kThreads;
     const int h = i / (D / 8);
-    const int c8 = i % (D / 8);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < G) v = reinterpret_cast<const uint4*>(a.q + (row0 + h) * D)[c8];
-    *reinterpret_cast<uint4*>(&q_lds[h * kQPad + 8 * c8]) = v;
+    qv[r] = (h < G) ? reinterpret_cast<const uint4*>(a.q + (row0 + h) * D)[i % (D / 8)]
+                    : make_uint4(0, 0, 0, 0);
+  }
+  auto page_at = [&](int j) {
+    PageRef pg;
+    int phys = __builtin_amdgcn_readlane(my_id, j);
+    pg.valid = min(PT, t1 - (t0 + (w + kWaves * j) * PT));
+    if (phys < 0 || phys >= a.num_pages) { phys = 0; pg.valid = 0; }   // read page 0, mask all
+    const uint16_t* page = layer_base + (int64_t)phys * a.page_elems;
+    pg.k = page + (int64_t)g * PT * D;
+    pg.v = page + (int64_t)(a.num_kv_heads + g) * PT * D;
+    return pg;
+  };
+  // One register buffer: the next chunk's K (V) loads follow QK (PV) of
+  // this chunk.
+  uint4 kA[2][8], vA[16];
+  const int n_chunks = 2 * my_pages;
+  PageRef cur = page_at(0);
+  if (n_chunks > 0) {
+    load_k(kA, cur, 0, lane);
+    load_v(vA, cur, 0, lane);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * kThreads;
+    *reinterpret_cast<uint4*>(&q_lds[(i / (D / 8)) * kQPad + 8 * (i % (D / 8))]) = qv[r];
   }
   __syncthreads();
 
@@ -218,72 +253,19 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < 16; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* layer_base = a.arena + a.layer_off;
-  const int32_t* trow = a.table + (int64_t)b * a.pt_stride;
-  const int first_page = (t0 - a.token_begin) / PT;
-  const int n_pages = (t1 > t0) ? (t1 - t0 + PT - 1) / PT : 0;
-  // this wave's pages: w, w + 4, ...
-  const int my_pages = (n_pages > w) ? (n_pages - w + kWaves - 1) / kWaves : 0;
-
-  // Page ids of this wave's pages (at most 64: split_tokens <= 16384): lane j
-  // holds the id of the wave's page j, fetched once before the loop and read
-  // with readlane, so no dependent global load sits in front of K/V loads.
-  const int my_id = (lane < my_pages) ? trow[first_page + w + kWaves * lane] : 0;
-  auto page_at = [&](int j) {
-    PageRef pg;
-    int phys = __builtin_amdgcn_readlane(my_id, j);
-    pg.valid = min(PT, t1 - (t0 + (w + kWaves * j) * PT));
-    if (phys < 0 || phys >= a.num_pages) { phys = 0; pg.valid = 0; }   // read page 0, mask all
-    const uint16_t* page = layer_base + (int64_t)phys * a.page_elems;
-    pg.k = page + (int64_t)g * PT * D;
-    pg.v = page + (int64_t)(a.num_kv_heads + g) * PT * D;
-    return pg;
-  };
-
-  // Two register buffers (A: tokens 0-31, B: tokens 32-63 of a page).  While
-  // a chunk computes, the other chunk's loads and the next page's loads of
-  // the buffer just consumed are in flight.
-  uint4 kA[2][8], kB[2][8], vA[16], vB[16];
-  if constexpr (kRing == 2) {
-    if (my_pages > 0) {
-      PageRef cur = page_at(0);
-      load_k(kA, cur, 0, lane);
-      load_v(vA, cur, 0, lane);
-      load_k(kB, cur, 32, lane);
-      load_v(vB, cur, 32, lane);
-      for (int j = 0; j + 1 < my_pages; ++j) {
-        const PageRef nxt = page_at(j + 1);
-        chunk<true>(kA, vA, acc, m, lsum, qrow, min(32, cur.valid), a.scale_log2, q, lane,
-                    nxt, 0);
-        chunk<true>(kB, vB, acc, m, lsum, qrow, max(0, cur.valid - 32), a.scale_log2, q, lane,
-                    nxt, 32);
-        cur = nxt;
-      }
-      chunk<false>(kA, vA, acc, m, lsum, qrow, min(32, cur.valid), a.scale_log2, q, lane, cur,
-                   0);
-      chunk<false>(kB, vB, acc, m, lsum, qrow, max(0, cur.valid - 32), a.scale_log2, q, lane,
-                   cur, 32);
+  if (n_chunks > 0) {
+    int cbase = 0;
+    for (int ci = 0; ci + 1 < n_chunks; ++ci) {
+      const int ni = ci + 1;
+      const PageRef nxt = (ni & 1) ? cur : page_at(ni >> 1);
+      const int nbase = 32 * (ni & 1);
+      chunk<true>(kA, vA, acc, m, lsum, qrow, max(0, min(32, cur.valid - cbase)), a.scale_log2,
+                  q, lane, nxt, nbase);
+      cur = nxt;
+      cbase = nbase;
     }
-  } else {
-    // one buffer: the next chunk's K (V) loads follow QK (PV) of this chunk
-    const int n_chunks = 2 * my_pages;
-    if (n_chunks > 0) {
-      PageRef cur = page_at(0);
-      int cbase = 0;
-      load_k(kA, cur, 0, lane);
-      load_v(vA, cur, 0, lane);
-      for (int ci = 0; ci + 1 < n_chunks; ++ci) {
-        const int ni = ci + 1;
-        const PageRef nxt = (ni & 1) ? cur : page_at(ni >> 1);
-        const int nbase = 32 * (ni & 1);
-        chunk<true>(kA, vA, acc, m, lsum, qrow, max(0, min(32, cur.valid - cbase)), a.scale_log2,
-                    q, lane, nxt, nbase);
-        cur = nxt;
-        cbase = nbase;
-      }
-      chunk<false>(kA, vA, acc, m, lsum, qrow, max(0, min(32, cur.valid - cbase)), a.scale_log2, q,
-                   lane, cur, cbase);
-    }
+    chunk<false>(kA, vA, acc, m, lsum, qrow, max(0, min(32, cur.valid - cbase)), a.scale_log2, q,
+                 lane, cur, cbase);
   }
 
   // ---- this wave's (m, l, acc) into LDS
@@ -329,7 +311,7 @@ template <int G>
 hipError_t launch_g(const DecodeArgs& a, int batch, hipStream_t stream) {
   const int n_split = a.token_count / a.split_tokens;
   dim3 grid(n_split, a.num_kv_heads, batch);
-  hipLaunchKernelGGL((decode_mfma_kernel<G, PKV_MFMA_RING>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
