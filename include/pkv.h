@@ -299,6 +299,9 @@ int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
  * of the buffer it overwrites (that lease's consumer and write-back events),
  * the compute stream waits for the copy, and the write-back waits for the
  * compute stream's consumer event.  Only pkv_stager_retire blocks the host.
+ * Each window's copy is split in two: the first half on `copy`, the second
+ * on a stream the stager creates and owns (default priority, destroyed with
+ * the stager), so one copy's wait overlaps the other's transfer.
  *
  * Lifecycle.  pkv_lease_begin queues the copy of tokens
  * [window_begin, window_begin + window_tokens) of every request (runs of

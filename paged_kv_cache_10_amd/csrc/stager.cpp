@@ -4,9 +4,12 @@
 // ordering" and "Leases instead of buffers"; KV-cache engineering, "Staging
 // layers under a lease"; GPU memory management, "Staging as a lease").
 //
-// Ordering is on the device: the copy stream waits for the previous readers
-// of the buffer it overwrites, the compute stream waits for the copy, the
-// write-back stream waits for the compute stream's consumer event.  The host
+// Ordering is on the device: the copy streams wait for the previous readers
+// of the buffer they overwrite, the compute stream waits for the copies, the
+// write-back stream waits for the compute stream's consumer event.  Each
+// window's copy is split in two halves, one on the caller's copy stream and
+// one on a second copy stream the stager owns (default priority), so that one
+// copy engine's wait before a window overlaps the other's transfer.  The host
 // blocks only in pkv_stager_retire.  Any HIP failure quarantines the stager:
 // new leases are refused and nothing is released until a drain proves that
 // every queued copy and kernel finished.
@@ -27,7 +30,8 @@ namespace {
 int fail(int code, const char* msg) { return pkv::set_error(code, "%s", msg); }
 
 struct Buffer {
-  hipEvent_t copied = nullptr;     // H2D copy of the window done (copy stream)
+  hipEvent_t copied = nullptr;     // H2D copy of the window's first half done (copy stream)
+  hipEvent_t copied2 = nullptr;    // and of its second half (the stager's own copy stream)
   hipEvent_t consumed = nullptr;   // work of the lease on the compute stream done
   hipEvent_t written = nullptr;    // tail write-back done (write-back stream)
   bool has_readers = false;        // consumed / written recorded by a sealed lease
@@ -52,6 +56,7 @@ struct pkv_stager {
   int32_t num_buffers;
   int32_t* dev_tables;             // [num_buffers][max_batch][window_pages]
   hipStream_t copy, compute, writeback;
+  hipStream_t copy2 = nullptr;     // the stager's own second copy stream
   std::vector<Buffer> buffers;
   uint64_t generation = 0;         // leases begun so far
   bool open = false;               // a lease is begun and not yet sealed
@@ -121,17 +126,21 @@ PKV_API int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_
   std::vector<int32_t> t((size_t)need);
   for (int64_t i = 0; i < need; ++i) t[(size_t)i] = (int32_t)i;
   hipError_t e = hipMemcpy(dev_tables, t.data(), sizeof(int32_t) * (size_t)need, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&st->copy2, hipStreamNonBlocking);
   for (auto& bf : st->buffers) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bf.copied, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&bf.copied2, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bf.consumed, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bf.written, hipEventDisableTiming);
   }
   if (e != hipSuccess) {
     for (auto& bf : st->buffers) {
       if (bf.copied) (void)hipEventDestroy(bf.copied);
+      if (bf.copied2) (void)hipEventDestroy(bf.copied2);
       if (bf.consumed) (void)hipEventDestroy(bf.consumed);
       if (bf.written) (void)hipEventDestroy(bf.written);
     }
+    if (st->copy2) (void)hipStreamDestroy(st->copy2);
     delete st;
     return pkv::set_error(PKV_ERR_DEVICE, "stager setup failed: %s", hipGetErrorString(e));
   }
@@ -173,10 +182,12 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
   const int32_t k = (int32_t)(st->generation % (uint64_t)st->num_buffers);
   Buffer& bf = st->buffers[k];
   hipError_t e = hipSuccess;
-  // the previous readers of buffer k must finish before the copy overwrites it
+  // the previous readers of buffer k must finish before the copies overwrite it
   if (bf.has_readers) {
-    e = hipStreamWaitEvent(st->copy, bf.consumed, 0);
-    if (e == hipSuccess && bf.wrote_back) e = hipStreamWaitEvent(st->copy, bf.written, 0);
+    for (hipStream_t cs : {st->copy, st->copy2}) {
+      if (e == hipSuccess) e = hipStreamWaitEvent(cs, bf.consumed, 0);
+      if (e == hipSuccess && bf.wrote_back) e = hipStreamWaitEvent(cs, bf.written, 0);
+    }
     if (e != hipSuccess) return quarantine(st, e, "wait for the buffer's readers");
   }
   const uint64_t plb = st->staging->page_layer_bytes;
@@ -193,8 +204,14 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
       const int32_t h0 = host_table[(int64_t)b * pt_stride + first + i];
       int64_t run = 1;
       while (i + run < npg && host_table[(int64_t)b * pt_stride + first + i + run] == h0 + run) ++run;
+      // first half of the run on the copy stream, the rest on the second one
+      const int64_t half = (run + 1) / 2;
       e = hipMemcpyAsync(slab + (uint64_t)(dst0 + i) * plb, hslab + (uint64_t)h0 * plb,
-                         (size_t)(run * (int64_t)plb), hipMemcpyHostToDevice, st->copy);
+                         (size_t)(half * (int64_t)plb), hipMemcpyHostToDevice, st->copy);
+      if (e == hipSuccess && run > half)
+        e = hipMemcpyAsync(slab + (uint64_t)(dst0 + i + half) * plb,
+                           hslab + (uint64_t)(h0 + half) * plb,
+                           (size_t)((run - half) * (int64_t)plb), hipMemcpyHostToDevice, st->copy2);
       i += run;
     }
     if (ctx > window_begin && ctx <= (int64_t)window_begin + st->window_tokens) {
@@ -203,7 +220,9 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
     }
   }
   if (e == hipSuccess) e = hipEventRecord(bf.copied, st->copy);
+  if (e == hipSuccess) e = hipEventRecord(bf.copied2, st->copy2);
   if (e == hipSuccess) e = hipStreamWaitEvent(st->compute, bf.copied, 0);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st->compute, bf.copied2, 0);
   if (e != hipSuccess) return quarantine(st, e, "window copy");
   st->open = true;
   st->open_generation = ++st->generation;
@@ -259,6 +278,7 @@ PKV_API int pkv_stager_retire(pkv_stager* st, int64_t* receipts) {
   if (st->quarantined) {
     // drain: the copy and write-back queues, the compute queue, then the device
     e = hipStreamSynchronize(st->copy);
+    if (e == hipSuccess) e = hipStreamSynchronize(st->copy2);
     if (e == hipSuccess) e = hipStreamSynchronize(st->writeback);
     if (e == hipSuccess) e = hipStreamSynchronize(st->compute);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -269,6 +289,7 @@ PKV_API int pkv_stager_retire(pkv_stager* st, int64_t* receipts) {
     for (auto& bf : st->buffers) {
       if (!bf.has_readers) continue;
       e = hipEventSynchronize(bf.copied);
+      if (e == hipSuccess) e = hipEventSynchronize(bf.copied2);
       if (e == hipSuccess) e = hipEventSynchronize(bf.consumed);
       if (e == hipSuccess && bf.wrote_back) e = hipEventSynchronize(bf.written);
       if (e != hipSuccess) {
@@ -312,9 +333,11 @@ PKV_API int pkv_stager_destroy(pkv_stager* st) {
     return fail(PKV_ERR_BUSY, "leases are outstanding; retire the stager first (destroy never waits)");
   for (auto& bf : st->buffers) {
     (void)hipEventDestroy(bf.copied);
+    (void)hipEventDestroy(bf.copied2);
     (void)hipEventDestroy(bf.consumed);
     (void)hipEventDestroy(bf.written);
   }
+  (void)hipStreamDestroy(st->copy2);
   delete st;
   pkv::clear_error();
   return PKV_OK;
