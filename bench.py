@@ -325,6 +325,9 @@ def main():
     if args.copy_probe:
         res["copy_probe"] = copy_probe(dev, stream)
 
+    res["append"] = append_probe(w, dev, stream)
+    res["admission"] = admission_probe(w)
+
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, qs, args.cpu_seconds)
 
@@ -454,6 +457,63 @@ def host_staged(args, w, pool, arena, table, ctx, qs, ref_outs, ref_lses, T, spa
                      "peak_kind": "measured: plain 1 GiB pinned-to-device copy (faster of one "
                                   "copy and two halves on two streams)"},
     }
+
+
+def append_probe(w, dev, stream):
+    """pkv_append_kv, the step's new K/V rows into their pages, timed on a
+    pool of its own (one page per request) so the history stays untouched:
+    average time of one call for one layer over 200 calls."""
+    import torch
+    from paged_kv_cache_10_amd import pkv
+    B, Hkv = w.batch, w.num_kv_heads
+    arena = torch.zeros(B * w.page_layer_bytes // 2, dtype=torch.int16, device=dev)
+    pool = pkv.Pool(arena, 1, Hkv, w.head_dim, w.page_tokens)
+    table = torch.arange(B, dtype=torch.int32, device=dev).view(B, 1)
+    pos = torch.full((B,), 5, dtype=torch.int32, device=dev)
+    k = torch.randn((B, Hkv, w.head_dim), device=dev).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, w.head_dim), device=dev).to(torch.bfloat16)
+    for _ in range(10):
+        pkv.append_kv(pool, 0, table, pos, k, v, stream=stream)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(200):
+        pkv.append_kv(pool, 0, table, pos, k, v, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / 200
+    return {"us_per_layer": round(us, 2), "bytes_per_layer": B * Hkv * w.head_dim * 2 * 2,
+            "share_of_step_16_layers": None}
+
+
+def admission_probe(w, steps=200):
+    """pkv_admit_step on the host: this workload's requests as contexts whose
+    targets together exceed the pool, so every step reuses, reclaims and
+    refuses; average host time of one planned step."""
+    from paged_kv_cache_10_amd import pkv
+    PT = w.page_tokens
+    need = [-(-c // PT) for c in w.ctx_lens]
+    pool_pages = max(2 * len(need), sum(need) * 3 // 4)          # 3/4 of what all would need
+    a = pkv.Admission(pool_pages, PT)
+    for i, n in enumerate(need):
+        a.add(i, max(2, n * 2 // 3), burst=max(0, n // 3))
+    lengths = list(w.ctx_lens)
+    stride = max(need) + steps // PT + 2
+    t0 = time.perf_counter()
+    a.step(list(range(len(need))), lengths, stride)              # first fill of the pool
+    fill_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    for k in range(1, steps + 1):
+        active = [i for i in range(len(need)) if (i + k) % 3]   # a third idle each step
+        a.step(active, [lengths[i] + k for i in active], stride)
+    dt = time.perf_counter() - t0
+    c = a.counts()
+    a.close()
+    return {"us_per_step": round(dt / steps * 1e6, 1), "first_fill_ms": round(fill_ms, 2),
+            "contexts": len(need),
+            "pool_pages": pool_pages, "counts": c,
+            "note": "host time including the Python binding"}
 
 
 def copy_probe(dev, stream):

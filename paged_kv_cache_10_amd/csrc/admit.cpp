@@ -44,9 +44,16 @@ struct Ctx {
   int32_t target;
   int32_t burst;
   int64_t last_active = 0;      // step it was last active (0 = never)
-  std::map<int32_t, int32_t> pages;   // logical page -> device page
+  std::map<int32_t, int32_t> pages;   // logical page -> device page, oldest first
+  std::vector<int32_t> where;         // the same as a dense index (-1: not resident)
   std::set<int32_t> borrowed;         // device pages held beyond target via burst
   int32_t held() const { return (int32_t)pages.size(); }
+  bool has(int32_t lp) const { return lp < (int32_t)where.size() && where[(size_t)lp] >= 0; }
+  void put(int32_t lp, int32_t page) {
+    if (lp >= (int32_t)where.size()) where.resize((size_t)lp + 1, -1);
+    where[(size_t)lp] = page;
+    pages[lp] = page;
+  }
 };
 
 }  // namespace
@@ -88,6 +95,7 @@ int32_t drop(Ctx& c, int32_t lp) {
   auto it = c.pages.find(lp);
   const int32_t page = it->second;
   c.pages.erase(it);
+  c.where[(size_t)lp] = -1;
   c.borrowed.erase(page);
   return page;
 }
@@ -103,18 +111,25 @@ std::vector<Ctx*> victims_lra(pkv_admit* A, int32_t self) {
   return v;
 }
 
-// Oldest non-sink logical page of c satisfying pred, or -1.
-template <typename P>
-int32_t oldest_non_sink(const Ctx& c, P pred) {
-  for (const auto& kv : c.pages)
-    if (kv.first != 0 && pred(kv.first, kv.second)) return kv.first;
+// Oldest non-sink logical page of c below `limit`, or -1 (O(1): the map is
+// ordered by logical page).
+int32_t oldest_non_sink_below(const Ctx& c, int32_t limit) {
+  auto it = c.pages.upper_bound(0);
+  return (it != c.pages.end() && it->first < limit) ? it->first : -1;
+}
+
+// Oldest non-sink logical page of c holding a borrowed device page, or -1.
+int32_t oldest_borrowed(const Ctx& c) {
+  if (c.borrowed.empty()) return -1;
+  for (auto it = c.pages.upper_bound(0); it != c.pages.end(); ++it)
+    if (c.borrowed.count(it->second)) return it->first;
   return -1;
 }
 
 // A page for logical page lp of context c (see the file comment), or -1.
 int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo) {
   // 1. own page outside the window
-  const int32_t out = oldest_non_sink(c, [&](int32_t l, int32_t) { return l < window_lo; });
+  const int32_t out = oldest_non_sink_below(c, window_lo);
   if (out >= 0) {
     const int32_t page = drop(c, out);
     event(A, PKV_ADMIT_REUSE_OWN, c.id, c.id, page, lp);
@@ -130,15 +145,15 @@ int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo) {
   // 3. reclaim while below target: borrowed, above target, idle contexts
   if (c.held() < c.target) {
     for (Ctx* v : victims_lra(A, c.id)) {
-      if (v->borrowed.empty()) continue;
-      const int32_t vl = oldest_non_sink(*v, [&](int32_t, int32_t p) { return v->borrowed.count(p) > 0; });
+      const int32_t vl = oldest_borrowed(*v);
+      if (vl < 0) continue;
       const int32_t page = drop(*v, vl);
       event(A, PKV_ADMIT_RECLAIM_BORROWED, c.id, v->id, page, lp);
       return page;
     }
     for (Ctx* v : victims_lra(A, c.id)) {
       if (v->held() <= v->target) continue;
-      const int32_t vl = oldest_non_sink(*v, [](int32_t, int32_t) { return true; });
+      const int32_t vl = oldest_non_sink_below(*v, INT32_MAX);
       if (vl < 0) continue;
       const int32_t page = drop(*v, vl);
       event(A, PKV_ADMIT_RECLAIM_ABOVE_TARGET, c.id, v->id, page, lp);
@@ -150,6 +165,7 @@ int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo) {
       std::vector<int32_t> pages;
       for (const auto& kv : v->pages) pages.push_back(kv.second);
       v->pages.clear();
+      v->where.clear();
       v->borrowed.clear();
       for (auto it = pages.rbegin(); it != pages.rend(); ++it) A->free_list.push_back(*it);
       event(A, PKV_ADMIT_RECLAIM_IDLE, c.id, v->id, -1, -1);
@@ -160,7 +176,7 @@ int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo) {
     }
   }
   // 4. shrink from the own oldest non-sink page older than lp
-  const int32_t old = oldest_non_sink(c, [&](int32_t l, int32_t) { return l < lp; });
+  const int32_t old = oldest_non_sink_below(c, lp);
   if (old >= 0) {
     const int32_t page = drop(c, old);
     event(A, PKV_ADMIT_SHRINK_OWN, c.id, c.id, page, lp);
@@ -274,7 +290,7 @@ PKV_API int pkv_admit_step(pkv_admit* A, int32_t n, const int32_t* ctx_ids,
     std::vector<int32_t> want{0};
     for (int32_t lp = need - 1; lp >= lo; --lp) want.push_back(lp);
     for (int32_t lp : want) {
-      if (c.pages.count(lp)) continue;
+      if (c.has(lp)) continue;
       const int32_t page = acquire(A, c, lp, lo);
       if (page < 0) {
         if (lp == 0) {
@@ -283,7 +299,7 @@ PKV_API int pkv_admit_step(pkv_admit* A, int32_t n, const int32_t* ctx_ids,
         }
         break;
       }
-      c.pages[lp] = page;
+      c.put(lp, page);
       if (c.held() > c.target) c.borrowed.insert(page);
     }
     if (!refused[i] && c.held() < std::min(kFloor, need)) {
@@ -295,9 +311,9 @@ PKV_API int pkv_admit_step(pkv_admit* A, int32_t n, const int32_t* ctx_ids,
   for (int32_t i = 0; i < n; ++i) {
     const Ctx& c = A->ctxs[ctx_ids[i]];
     int32_t* row = table + (int64_t)i * pt_stride;
-    for (int32_t lp = 0; lp < pt_stride; ++lp) row[lp] = -1;
-    for (const auto& kv : c.pages)
-      if (kv.first < pt_stride) row[kv.first] = kv.second;
+    const int32_t known = std::min<int32_t>(pt_stride, (int32_t)c.where.size());
+    std::copy(c.where.begin(), c.where.begin() + known, row);
+    std::fill(row + known, row + pt_stride, -1);
     bool whole = row[0] >= 0;
     for (int32_t lp = lo_of[i]; lp < need_of[i] && whole; ++lp) whole = row[lp] >= 0;
     status[i] = refused[i] ? PKV_ADMIT_REFUSED_STEP : whole ? PKV_ADMIT_FULL : PKV_ADMIT_PARTIAL;
