@@ -2,8 +2,9 @@
 
 One step = one decode token for every request: for each of the 16 layers,
 pkv_decode_attention (split-KV tile partials) then pkv_merge_partials (FP32
-LSE merge); where LAUNCH says so, layer l's merge runs on a second stream
-while layer l+1 decodes, and the step ends when every merge has.  Default workload: 1 request x
+LSE merge) on the same stream (with --overlap, layer l's merge runs on a
+second stream while layer l+1 decodes, and the step ends when every merge
+has; the line reports the other schedule too).  Default workload: 1 request x
 262,144 tokens, 16 layers, 24 q / 4 KV heads, head_dim 256, bf16, 64-token
 pages in a 16 GiB arena in random physical order, 1 % of keys scaled by 4;
 each 32,768-token staging window of the history is split-KV eight ways into
@@ -78,12 +79,15 @@ def pmc_traffic(workload, tile, split, kernel):
 
 # Launch configuration timed for each workload (tile tokens; tokens per
 # work-group).  The full-size parity tests run exactly these.
-# `overlap`: layer l's merge runs on a second stream while layer l+1 decodes.
+# Every layer's merge follows its decode on the same stream, as a model whose
+# next layer needs this layer's output runs them; --overlap instead runs
+# layer l's merge on a second stream while layer l+1 decodes (the synthetic
+# layers are independent), and the line reports the other schedule as well.
 LAUNCH = {
-    "long262k": dict(tile=4096, split=4096, overlap=True),   # 32K windows split-KV 8 ways
-    "conc": dict(tile=1984, split=1984, overlap=False),      # 16 full 1,984-token tiles per request
-    "mixed": dict(tile=2048, split=2048, overlap=True),
-    "tiny": dict(tile=1024, split=1024, overlap=False),
+    "long262k": dict(tile=4096, split=4096),   # 32K windows split-KV 8 ways
+    "conc": dict(tile=1984, split=1984),       # 16 full 1,984-token tiles per request
+    "mixed": dict(tile=2048, split=2048),
+    "tiny": dict(tile=1024, split=1024),
 }
 
 
@@ -108,7 +112,10 @@ def parse():
     ap.add_argument("--kernel", default="mfma", choices=["mfma", "valu"])
     ap.add_argument("--staged", action="store_true",
                     help="decode each 32,768-token staging window with its own call")
-    ap.add_argument("--serial", action="store_true", help="merge on the decode stream")
+    ap.add_argument("--serial", action="store_true",
+                    help="merge on the decode stream (the default)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="merge layer l on a second stream while layer l+1 decodes")
     ap.add_argument("--host-staged", action="store_true",
                     help="history in pinned host memory, staged per 32K window under leases")
     ap.add_argument("--compact-older", action="store_true",
@@ -145,7 +152,7 @@ def main():
     launch = LAUNCH.get(args.workload, {})
     w.tile_tokens = args.tile or launch.get("tile", w.tile_tokens)
     args.split = args.split or launch.get("split", 0)
-    overlap = launch.get("overlap", False) and not args.serial
+    overlap = args.overlap and not args.serial
     T = w.tile_tokens
     B, Hq, Hkv, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
 
@@ -222,16 +229,13 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / K
-    # the same steps with every merge on the decode stream, as a model whose
-    # next layer needs this layer's output would run them
-    ms_serial = ms_step
-    if overlap:
-        e0.record(stream)
-        for k in range(K):
-            step(overlap=False)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_serial = e0.elapsed_time(e1) / K
+    # the same steps in the other merge schedule, for comparison
+    e0.record(stream)
+    for k in range(K):
+        step(overlap=not overlap)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_other = e0.elapsed_time(e1) / K
     # roofline: K more steps with an event pair around every decode call
     ev_dec = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(L)] for _ in range(K)]
@@ -242,6 +246,7 @@ def main():
     dec_avg_ms = float(np.mean(dec_ms))
 
     # the overlapped schedule against a serialized recompute on one stream
+    step(overlap=True)
     torch.cuda.synchronize()
     ref_o, ref_l = outs.clone(), lses.clone()
     for layer in range(L):
@@ -313,9 +318,10 @@ def main():
         },
         "setup_s": round(t_gen, 1),
         "overlapped_equals_serial_bitwise": self_check,
-        "serial_merges": {"ms_per_step": round(ms_serial, 4),
-                          "value": round(kv_bytes_step / (ms_serial * 1e-3) / 1e9, 1),
-                          "hbm_frac": round(kv_bytes_step / (ms_serial * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        ("serial_merges" if overlap else "overlapped_merges"): {
+            "ms_per_step": round(ms_other, 4),
+            "value": round(kv_bytes_step / (ms_other * 1e-3) / 1e9, 1),
+            "hbm_frac": round(kv_bytes_step / (ms_other * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
 
     if ceiling is not None:
@@ -326,6 +332,7 @@ def main():
         res["copy_probe"] = copy_probe(dev, stream)
 
     res["append"] = append_probe(w, dev, stream)
+    res["append"]["share_of_step"] = round(L * res["append"]["us_per_layer"] * 1e-3 / ms_step, 4)
     res["admission"] = admission_probe(w)
 
     if not args.no_cpu_baseline:
@@ -483,8 +490,7 @@ def append_probe(w, dev, stream):
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / 200
-    return {"us_per_layer": round(us, 2), "bytes_per_layer": B * Hkv * w.head_dim * 2 * 2,
-            "share_of_step_16_layers": None}
+    return {"us_per_layer": round(us, 2), "bytes_per_layer": B * Hkv * w.head_dim * 2 * 2}
 
 
 def admission_probe(w, steps=200):
@@ -599,11 +605,8 @@ def compact_older(args, w, pool, table, ctx, qs, ref_outs, ref_lses):
     nb = max(pkv.decode_workspace_bytes(B, Hq, Sc * T, T, D, 0, S),
              pkv.decode_workspace_bytes(B, Hq, Se * Te, Te, D, 0, Se_))
     ws = torch.zeros(max(16, nb) // 4 + 4, device=dev)
-    merge_stream = torch.cuda.Stream()
-    decoded = [torch.cuda.Event() for _ in range(L)]
-    merged = torch.cuda.Event()
 
-    def step(evs=None, overlap=overlap):
+    def step(evs=None):
         for layer in range(L):
             if evs is not None:
                 evs[layer][0].record(stream)
@@ -614,11 +617,7 @@ def compact_older(args, w, pool, table, ctx, qs, ref_outs, ref_lses):
             pkv.decode_attention(pool, layer, qs[layer], det, dec, 0, Se * Te, Te, w.scale,
                                  po[layer], pl[layer], workspace=ws, split_tokens=Se_,
                                  slot_offset=Sc, stream=stream)
-            decoded[layer].record(stream)
-            merge_stream.wait_event(decoded[layer])
-            pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=merge_stream)
-        merged.record(merge_stream)
-        stream.wait_event(merged)
+            pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=stream)
 
     for _ in range(args.warmup):
         step()
