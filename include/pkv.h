@@ -222,7 +222,8 @@ int pkv_page_table_write(const pkv_pool* pool, const int32_t* host_table,
 typedef struct pkv_decode_opts {
   int32_t kernel;        /* 0 default, 1 VALU (fdot2 + FP32 FMA), 2 MFMA (16x16x32 bf16) */
   int32_t split_tokens;  /* 0 default; else tokens per work-group, a multiple of 64 dividing
-                            tile_tokens.  The split is a pure function of these options and
+                            tile_tokens, at most 16384 for the MFMA kernel and compact
+                            pools (PKV_ERR_INVALID_ARG beyond).  The split is a pure function of these options and
                             tile_tokens, never of batch, lengths or the device, so staged and
                             resident calls with the same options agree bit for bit. */
   int32_t slot_offset;   /* 0 default; added to every slot the call writes, so the runs of

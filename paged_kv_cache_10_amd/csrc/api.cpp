@@ -48,6 +48,7 @@ int ok() {
 }
 
 constexpr int kDefaultSplit = 2048;  // tokens per work-group unless the caller says otherwise
+constexpr int kMaxMfmaSplit = 64 * 4 * 64;   // 64 pages per wave x 4 waves x 64 tokens
 
 int check_geom(const pkv_geom* g) {
   if (!g) return fail(PKV_ERR_INVALID_ARG, "geom is NULL");
@@ -370,6 +371,12 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
 
   int split = 0;
   if (int rc = split_for(tile_tokens, opts, &split)) return rc;
+  // the matrix-core kernels hold one page id per lane of a wave: at most 64
+  // pages per wave, 4 waves per work-group
+  if (kernel == 2 && split > kMaxMfmaSplit)
+    return fail(PKV_ERR_INVALID_ARG,
+                "opts.split_tokens = %d exceeds %d tokens per work-group of the MFMA and compact "
+                "kernels", split, kMaxMfmaSplit);
   uint64_t need = 0;
   if (int rc = pkv_decode_workspace_bytes(batch, num_q_heads, G.head_dim, token_count, tile_tokens,
                                           opts, &need))

@@ -176,6 +176,7 @@ def decode_raw(pool, **kw):
     (dict(ws=0, tile=4096, slots=1), -4, "workspace"),          # 2,048-token splits
     (dict(ws_bytes=100, tile=4096, slots=1), -4, "workspace"),
     (dict(split=100), -1, "split_tokens"),
+    (dict(split=32768, tile=32768, count=32768, slots=1, pt_stride=512), -1, "16384"),
     (dict(batch=-1), -1, "batch"),
 ])
 def test_decode_arguments_are_refused_on_the_host(kw, code, needle):
