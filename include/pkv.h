@@ -374,7 +374,7 @@ int pkv_stager_destroy(pkv_stager* stager);
  *   status  int32 [n] out: PKV_ADMIT_FULL, PKV_ADMIT_PARTIAL or
  *           PKV_ADMIT_REFUSED_STEP.
  * Every fill and reclamation is counted (pkv_admit_get_counts) and logged
- * (pkv_admit_events drains the log). */
+ * (pkv_admit_events drains the log; it grows until drained). */
 enum {
   PKV_ADMIT_REUSE_OWN = 1, PKV_ADMIT_TAKE_FREE = 2, PKV_ADMIT_RECLAIM_BORROWED = 3,
   PKV_ADMIT_RECLAIM_ABOVE_TARGET = 4, PKV_ADMIT_RECLAIM_IDLE = 5, PKV_ADMIT_SHRINK_OWN = 6,
