@@ -128,8 +128,8 @@ def parse():
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy (the PMC calibration kernel)")
-    ap.add_argument("--read-probe", action="store_true",
-                    help="also report the measured HBM read ceiling (runs probe_read first)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the measured HBM read ceiling (probe_read, run first as a child)")
     return ap.parse_args()
 
 
@@ -139,7 +139,7 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(no multi-GPU path exists)", file=sys.stderr)
         return 2
-    ceiling = read_probe() if args.read_probe else None
+    ceiling = None if args.no_read_probe else read_probe()
     import torch
     from paged_kv_cache_10_amd import inputs as I
     from paged_kv_cache_10_amd import pkv
@@ -267,6 +267,10 @@ def main():
         return 0
     if args.compact_older:
         res = compact_older(args, w, pool, table, ctx, qs, outs, lses)
+        if ceiling is not None:
+            res["read_ceiling"] = ceiling
+            res["roofline"]["frac_of_measured_ceiling"] = round(
+                res["roofline"]["achieved"] / ceiling["blocks_GBs"], 4)
         if args.copy_probe:
             res["copy_probe"] = copy_probe(dev, stream)
         print(json.dumps(res), flush=True)
@@ -682,10 +686,13 @@ def compact_older(args, w, pool, table, ctx, qs, ref_outs, ref_lses):
 
 
 def read_probe():
-    """Measured HBM read ceiling: probe_read, run as a child process."""
+    """Measured HBM read ceiling: probe_read, run as a child process before
+    this process touches the GPU; None if the probe is not built."""
     import subprocess
     exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_10_amd",
                        "probe_read")
+    if not os.path.exists(exe):
+        return None
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout
     return json.loads(out.strip().splitlines()[-1])
 

@@ -317,6 +317,20 @@ def test_two_runs_with_their_own_tilings(gpu):
     runs.check(got, runs.oracle(0, 3584, etile=512))
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (48, 4), (64, 4), (16, 2)])
+def test_compact_query_group_sizes(gpu, hq, hkv):
+    """The compact kernel for query groups of 1, 2, 4, 8, 12 and 16 heads per
+    KV head, lengths around page edges (every full page compact, the partial
+    last page exact), poisoned exact padding."""
+    w = I.Workload("cgroups", seed=66, ctx_lens=[130, 2049, 777], num_layers=1,
+                   tile_tokens=1024, num_q_heads=hq, num_kv_heads=hkv)
+    case = Case(w, fill=I.BF16_QNAN)
+    runs = Runs(case, [n // 64 * 64 for n in w.ctx_lens])
+    for split in (0, 256):
+        got = runs.decode(0, 1024, split)
+        runs.check(got, runs.oracle(0, 1024))
+
+
 def test_compact_decode_is_deterministic_and_agrees_across_splits(gpu):
     w = I.Workload("cdet", seed=64, ctx_lens=[20000, 9000], num_layers=1, tile_tokens=4096,
                    arena_pages=500)
