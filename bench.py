@@ -38,18 +38,18 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "805167465b2b792b27851ddec9ae80e22d5abaa245b7be968c0d46d4b1b84b5a",
+    "source_sha256": "10d0665c375201d9d9dc80d4a5957b45da749f03dbba8fb7ac076ae98afc04da",
     "workload": "long262k", "tile": 4096, "split": 4096,
-    "fetch_kib": 524445.7, "fetch_scale": 1048576 / 524317.7,
-    "write_kib": 1584.1, "write_scale": 1.0,
+    "fetch_kib": 524475.7, "fetch_scale": 1048576 / 524314.1,
+    "write_kib": 1584.05, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/device.h")
 
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "f20f502cc31174054d1de7161b0c8c4b7f3984a0190f1f950cc53756a0d1a4d2",
-    "fetch_kib": 229775.5, "fetch_scale": 1048576 / 524303.9,
+    "source_sha256": "f57d057e001aa057c672433e6da8181252d00d70dd3a2bd970315e88787ba6c0",
+    "fetch_kib": 230026.8, "fetch_scale": 1048576 / 524299.9,
     "write_kib": 1584.0, "write_scale": 1.0,
 }
 FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_amd/csrc/compact.h",
@@ -86,7 +86,7 @@ def pmc_traffic(workload, tile, split, kernel):
 LAUNCH = {
     "long262k": dict(tile=4096, split=4096),   # 32K windows split-KV 8 ways
     "conc": dict(tile=1984, split=1984),       # 16 full 1,984-token tiles per request
-    "mixed": dict(tile=2048, split=2048),
+    "mixed": dict(tile=1728, split=1728),     # 1,020 work-groups: the best measured shape
     "tiny": dict(tile=1024, split=1024),
 }
 

@@ -169,7 +169,7 @@ void decode_fp8_kernel(CompactDecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
-  const int split = blockIdx.x;
+  const int split = rotated_split();
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;

@@ -164,7 +164,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
-  const int split = blockIdx.x;
+  const int split = rotated_split();
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;

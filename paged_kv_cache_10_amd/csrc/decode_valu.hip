@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
-  const int split = blockIdx.x;
+  const int split = rotated_split();
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;

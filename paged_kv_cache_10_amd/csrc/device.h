@@ -46,6 +46,18 @@ __device__ __forceinline__ int v_piece(int d, int u) {
   return ((u >> 2) * 16 + (d >> 4)) * 64 + (u & 3) * 16 + (d & 15);
 }
 
+// XCD-aware placement.  Work-groups are dealt to the 8 XCDs round-robin by
+// linear id, and every (request, KV head) row of the grid starts at split 0,
+// which is often the row's only non-empty split; with a row length that is a
+// multiple of 8 every row's split 0 would land on one XCD.  Rotating each
+// row's splits by a row-dependent amount spreads them; a split's arithmetic
+// does not depend on which work-group runs it.
+__device__ __forceinline__ int rotated_split() {
+  const unsigned row = blockIdx.y + gridDim.y * blockIdx.z;
+  const unsigned rot = (row & 7u) % gridDim.x;
+  return (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
