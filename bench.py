@@ -123,6 +123,9 @@ def parse():
                          "pages converted on the GPU; prints its own JSON line")
     ap.add_argument("--buffers", type=int, default=2,
                     help="staging buffers of the --host-staged mode")
+    ap.add_argument("--merge-stress", action="store_true",
+                    help="time pkv_merge_partials alone on 64 x 24 rows x 256 partials; "
+                         "prints its own JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
@@ -140,6 +143,9 @@ def main():
               "(no multi-GPU path exists)", file=sys.stderr)
         return 2
     ceiling = None if args.no_read_probe else read_probe()
+    if args.merge_stress:
+        print(json.dumps(merge_stress(args, ceiling)), flush=True)
+        return 0
     import torch
     from paged_kv_cache_10_amd import inputs as I
     from paged_kv_cache_10_amd import pkv
@@ -229,6 +235,15 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / K
+    # five more passes of K steps: median and spread of the step time
+    passes = []
+    for _ in range(5):
+        e0.record(stream)
+        for k in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        passes.append(e0.elapsed_time(e1) / K)
     # the same steps in the other merge schedule, for comparison
     e0.record(stream)
     for k in range(K):
@@ -307,6 +322,10 @@ def main():
         "tokens_per_s": round(tok_s, 2),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv_bytes_step,
+        "total_bytes_per_step": total_bytes_step(w, T, ws_bytes > 0),
+        "passes": {"n": len(passes), "ms_per_step_median": round(float(np.median(passes)), 4),
+                   "ms_per_step_min": round(min(passes), 4),
+                   "ms_per_step_max": round(max(passes), 4)},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_mfma_kernel" if args.kernel == "mfma" else "decode_valu_kernel",
@@ -468,6 +487,78 @@ def host_staged(args, w, pool, arena, table, ctx, qs, ref_outs, ref_lses, T, spa
                      "peak_kind": "measured: plain 1 GiB pinned-to-device copy (faster of one "
                                   "copy and two halves on two streams)"},
     }
+
+
+def merge_stress(args, ceiling):
+    """The FP32 merge alone on the merge-stress shape: 64 requests x 24 heads
+    x 256 partials of 256 channels, lse uniform in [-40, 40], 10 % of the
+    partials empty (lse = -inf, output 0); seeded, generated on the device.
+    Bytes per call: every partial output and lse read, out and lse written."""
+    import torch
+    from paged_kv_cache_10_amd import pkv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pkv.lib()
+    B, H, S, D = 64, 24, 256, 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    po = torch.randn((B, H, S, D), generator=g, device=dev)
+    pl = torch.rand((B, H, S), generator=g, device=dev) * 80.0 - 40.0
+    empty = torch.rand((B, H, S), generator=g, device=dev) < 0.1
+    pl[empty] = float("-inf")
+    po[empty] = 0.0
+    out = torch.empty((B, H, D), device=dev)
+    lse = torch.empty((B, H), device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pkv.merge_partials(po, pl, out, lse, stream=stream)
+    K = max(args.steps, 20)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(K):
+        pkv.merge_partials(po, pl, out, lse, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    nbytes = (po.numel() + pl.numel() + out.numel() + lse.numel()) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "FP32 LSE merge GB/s on the merge-stress shape (64 x 24 x 256 partials)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "merge stress: 64 x 24 rows x 256 partials x 256 channels, lse "
+                               "U[-40, 40], 10 % empty"},
+        "bytes_per_call": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "merge_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5),
+                     "traffic": None},
+    }
+    if ceiling is not None:
+        res["read_ceiling"] = ceiling
+    return res
+
+
+def total_bytes_step(w, T, finalize):
+    """Every byte one step moves, not only KV: per layer the KV history, q,
+    the page-table entries read, the tile partials written (and, where a
+    tile has several splits, the split partials written and read back), the
+    partials read by the merge, and out and lse written."""
+    PT = w.page_tokens
+    rows = w.batch * w.num_q_heads
+    slots = -(-w.max_ctx // T)
+    pages = sum(-(-c // PT) for c in w.ctx_lens)
+    per_layer = (w.kv_bytes_per_step // w.num_layers
+                 + rows * w.head_dim * 2                        # q (bf16)
+                 + pages * 4                                    # page-table entries
+                 + 2 * rows * slots * (w.head_dim + 1) * 4      # partials written, then read
+                 + rows * (w.head_dim + 1) * 4)                 # out + lse
+    if finalize:
+        per_layer += 2 * rows * slots * (w.head_dim + 1) * 4    # split partials, written and read
+    return per_layer * w.num_layers
 
 
 def append_probe(w, dev, stream):
@@ -739,7 +830,19 @@ def cpu_baseline(w, qs, budget_s):
                   f"{w.batch} request(s), all heads, float64 one-pass), scaled x{w.num_layers / layers:.1f}",
         "seconds": round(spent, 2),
         "kv_GBs_equiv": round(w.kv_bytes_per_step / s_per_step / 1e9, 3),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -7,8 +7,9 @@
 //   * the final merge of every slot of a row into one output (pkv_merge_partials);
 //   * the tile finalize inside pkv_decode_attention, which merges the fixed
 //     groups of split partials that make up one tile.
-// Four waves own one (row, output slot), 64 channels each (one per lane, so
-// more of the GPU's load queues work on a row), and each walks its input
+// Two waves own one (row, output slot), 128 channels each (two per lane, so
+// more of the GPU's load queues work on a row and every load is 512
+// contiguous bytes), and each walks its input
 // slots in increasing order with one accumulator per channel, so the result
 // is independent of scheduling, an empty slot (lse = -inf) contributes
 // exactly nothing and a lone slot merges to itself bit for bit.
@@ -19,19 +20,21 @@ namespace pkv {
 
 namespace {
 
-constexpr int kMergeThreads = 64;     // one wave; lane i owns channel 64 * quarter + i
+constexpr int kMergeThreads = 64;     // one wave; lane i owns channels 128 * half + 2i, +1
+constexpr int kMergeParts = kHeadDim / 128;   // waves per (row, output slot)
 constexpr int kMergeUnroll = 32;      // input slots whose loads are in flight together
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int row = blockIdx.x;
   const int j = blockIdx.y;
-  const int quarter = blockIdx.z;
+  const int part = blockIdx.z;
   const int lane = threadIdx.x;
   const int t0 = j * a.group;
   const int cnt = min(a.group, a.in_slots - t0);
 
   const float* lse_in = a.in_lse + (int64_t)row * a.in_slots + t0;
-  const float* o_in = a.in_o + ((int64_t)row * a.in_slots + t0) * kHeadDim + 64 * quarter + lane;
+  const float2* o_in = reinterpret_cast<const float2*>(
+      a.in_o + ((int64_t)row * a.in_slots + t0) * kHeadDim + 128 * part) + lane;
 
   // M = max_t lse_t over the group.
   float m = -INFINITY;
@@ -39,10 +42,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
 
   const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
-  float* o_out = a.out_o + orow * kHeadDim + 64 * quarter + lane;
+  float2* o_out = reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part) + lane;
   if (m == -INFINITY) {                       // every slot empty
-    *o_out = 0.f;
-    if (quarter == 0 && lane == 0) a.out_lse[orow] = -INFINITY;
+    *o_out = make_float2(0.f, 0.f);
+    if (part == 0 && lane == 0) a.out_lse[orow] = -INFINITY;
     return;
   }
 
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   // (one exp per lane, all in parallel), then the slots are summed in
   // increasing order with each weight read from its lane; the output loads
   // go out kMergeUnroll at a time ahead of their use.
-  float acc = 0.f;
+  float2 acc = make_float2(0.f, 0.f);
   float wsum = 0.f;
   for (int c0 = 0; c0 < cnt; c0 += kMergeThreads) {
     const int nc = min(kMergeThreads, cnt - c0);
@@ -60,28 +63,30 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       const int t = c0 + sb * kMergeUnroll;
       const int n = min(kMergeUnroll, cnt - t);
       if (n <= 0) break;
-      float o[kMergeUnroll];
+      float2 o[kMergeUnroll];
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) o[u] = (u < n) ? o_in[(int64_t)(t + u) * kHeadDim] : 0.f;
+      for (int u = 0; u < kMergeUnroll; ++u)
+        o[u] = (u < n) ? o_in[(int64_t)(t + u) * (kHeadDim / 2)] : make_float2(0.f, 0.f);
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), sb * kMergeUnroll + u));
         if (w != 0.f) {                        // uniform across the wave
-          acc = fmaf(w, o[u], acc);
+          acc.x = fmaf(w, o[u].x, acc.x);
+          acc.y = fmaf(w, o[u].y, acc.y);
           wsum += w;
         }
       }
     }
   }
-  *o_out = acc / wsum;
-  if (quarter == 0 && lane == 0) a.out_lse[orow] = m + logf(wsum);
+  *o_out = make_float2(acc.x / wsum, acc.y / wsum);
+  if (part == 0 && lane == 0) a.out_lse[orow] = m + logf(wsum);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t stream) {
   if (rows <= 0 || a.n_out <= 0) return hipSuccess;
-  dim3 grid(rows, a.n_out, kHeadDim / 64);
+  dim3 grid(rows, a.n_out, kMergeParts);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
