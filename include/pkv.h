@@ -290,7 +290,11 @@ int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
  * management, "Staging as a lease").
  *
  * The host arena has the layout of a pool with `host_layers` layers and the
- * staging pool's head shape: host[layer][page][K|V][kv_head][block].  The
+ * staging pool's head shape: host[layer][page][K|V][kv_head][block].  With
+ * a compact staging pool it has the compact layout instead (codes of every
+ * layer, then their scales) and each window's scales are copied with its
+ * codes; compact pages are immutable, so a seal with write_back_tail is
+ * refused.  The
  * stager owns `num_buffers` staging buffers in layer 0 of the staging pool,
  * each of max_batch x window_tokens/64 pages, and three caller streams:
  *   copy       host -> device window copies;

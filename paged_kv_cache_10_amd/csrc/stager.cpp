@@ -55,6 +55,10 @@ struct pkv_stager {
   int32_t window_pages;
   int32_t num_buffers;
   int32_t* dev_tables;             // [num_buffers][max_batch][window_pages]
+  bool compact = false;            // compact (E4M3) pages: codes, plus a scale run per copy
+  uint64_t scale_bytes = 0;        // scales of one compact (layer, page)
+  char* host_scales = nullptr;     // scale region of the host arena
+  char* staging_scales = nullptr;  // scale region of the staging pool (its layer 0)
   hipStream_t copy, compute, writeback;
   hipStream_t copy2 = nullptr;     // the stager's own second copy stream
   std::vector<Buffer> buffers;
@@ -84,12 +88,12 @@ PKV_API int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_
   if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!staging) return fail(PKV_ERR_INVALID_ARG, "staging pool is NULL");
-  if (staging->format != PKV_FORMAT_BF16)
-    return fail(PKV_ERR_INVALID_ARG, "the staging pool must hold exact (bf16) pages");
   if (!host_arena || !dev_tables) return fail(PKV_ERR_INVALID_ARG, "host_arena or dev_tables is NULL");
   if (host_layers < 1) return fail(PKV_ERR_INVALID_ARG, "host_layers must be >= 1");
-  const uint64_t plb = staging->page_layer_bytes;
-  const uint64_t host_page_bytes = plb * (uint64_t)host_layers;
+  const bool compact = staging->format == PKV_FORMAT_E4M3;
+  const uint64_t plb = staging->page_layer_bytes;   // codes only, for a compact pool
+  const uint64_t sb = compact ? 2ull * (uint64_t)staging->geom.num_kv_heads * 4ull : 0ull;
+  const uint64_t host_page_bytes = (plb + sb) * (uint64_t)host_layers;
   if (host_bytes == 0 || host_bytes % host_page_bytes)
     return pkv::set_error(PKV_ERR_INVALID_ARG,
                           "host_bytes = %llu must be a positive whole number of %llu-byte pages",
@@ -117,6 +121,12 @@ PKV_API int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_
   st->window_pages = wpp;
   st->num_buffers = num_buffers;
   st->dev_tables = dev_tables;
+  st->compact = compact;
+  st->scale_bytes = sb;
+  if (compact) {
+    st->host_scales = st->host + (uint64_t)host_layers * (uint64_t)st->host_pages * plb;
+    st->staging_scales = static_cast<char*>(staging->base) + staging->scale_offset;
+  }
   st->copy = static_cast<hipStream_t>(copy_stream);
   st->compute = static_cast<hipStream_t>(compute_stream);
   st->writeback = static_cast<hipStream_t>(writeback_stream);
@@ -212,6 +222,12 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
         e = hipMemcpyAsync(slab + (uint64_t)(dst0 + i + half) * plb,
                            hslab + (uint64_t)(h0 + half) * plb,
                            (size_t)((run - half) * (int64_t)plb), hipMemcpyHostToDevice, st->copy2);
+      if (e == hipSuccess && st->compact)                    // the run's scales
+        e = hipMemcpyAsync(st->staging_scales + (uint64_t)(dst0 + i) * st->scale_bytes,
+                           st->host_scales + ((uint64_t)layer * (uint64_t)st->host_pages +
+                                              (uint64_t)h0) * st->scale_bytes,
+                           (size_t)((uint64_t)run * st->scale_bytes), hipMemcpyHostToDevice,
+                           st->copy);
       i += run;
     }
     if (ctx > window_begin && ctx <= (int64_t)window_begin + st->window_tokens) {
@@ -245,6 +261,8 @@ PKV_API int pkv_lease_seal(pkv_stager* st, const pkv_lease* lease, int32_t write
   if (!st->open || lease->generation != st->open_generation || lease->buffer != st->open_buffer)
     return pkv::set_error(PKV_ERR_LEASE, "lease %llu is not the open lease; a lease is sealed "
                           "only by its own handle", (unsigned long long)lease->generation);
+  if (write_back_tail && st->compact)
+    return fail(PKV_ERR_INVALID_ARG, "compact pages are immutable: nothing to write back");
   Buffer& bf = st->buffers[st->open_buffer];
   hipError_t e = hipEventRecord(bf.consumed, st->compute);
   bool wrote = false;

@@ -9,6 +9,7 @@ import torch
 from paged_kv_cache_10_amd import inputs as I
 from paged_kv_cache_10_amd import pkv
 import oracle
+from oracle import compact as C
 
 OUT_TOL = 2e-3     # max abs error on outputs
 LSE_TOL = 1e-4     # abs error on log-sum-exp
@@ -148,3 +149,148 @@ def check_layer(case, layer, got, ref, tile=None):
 
 def same_bits(a, b):
     return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------
+# compact older pages
+
+
+BLOCK = 64 * 256
+
+
+def kv_bits(case, layer, b):
+    """bf16 bit patterns [Hkv, ctx, 256] of request b's history."""
+    if case.host:
+        return I.draw_kv(case.w, layer, b)
+    k, v = I.device_kv(case.w, layer, b, DEV)
+    return (k.view(torch.int16).cpu().numpy().view(np.uint16),
+            v.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+class Runs:
+    """An exact Case plus a compact pool holding the first compact[b] tokens
+    (whole pages) of every request, converted on the GPU; the exact run's
+    table rows start at the first exact page."""
+
+    def __init__(self, case, compact_tokens, seed=0, spare=3):
+        w = self.w = case.w
+        self.case = case
+        self.c = np.array(compact_tokens, dtype=np.int32)
+        assert all(c % 64 == 0 and 0 <= c <= n for c, n in zip(self.c, w.ctx_lens))
+        n_pages = self.c // 64
+        total = int(n_pages.sum())
+        P = total + spare
+        cpb = pkv.compact_page_bytes(w.num_layers, w.num_kv_heads)
+        self.arena = torch.zeros(P * cpb, dtype=torch.uint8, device=DEV)
+        self.pool = pkv.Pool(self.arena, w.num_layers, w.num_kv_heads, compact=True)
+        assert pkv.pool_format(self.pool) == "e4m3" and self.pool.num_pages == P
+        ids = np.random.default_rng(1000 + seed).permutation(P)[:total].astype(np.int32)
+        width = case.table.shape[1]
+        self.ctable = np.full((w.batch, width), -1, np.int32)
+        self.etable = np.full((w.batch, width), -1, np.int32)
+        src, dst, k = [], [], 0
+        for b in range(w.batch):
+            for i in range(n_pages[b]):
+                src.append(case.table[b, i])
+                dst.append(ids[k])
+                self.ctable[b, i] = ids[k]
+                k += 1
+            rest = case.table[b, n_pages[b]:]
+            rest = rest[rest >= 0]
+            self.etable[b, :rest.size] = rest
+        self.src = np.array(src, np.int32)
+        self.dst = np.array(dst, np.int32)
+        self.crc = torch.zeros(max(total, 1), dtype=torch.int32, device=DEV)
+        if total:
+            pkv.compact_convert(case.pool, self.pool, torch.from_numpy(self.src).to(DEV),
+                                torch.from_numpy(self.dst).to(DEV), self.crc[:total])
+        self.cctx = self.c.copy()
+        self.ectx = (np.array(w.ctx_lens, np.int32) - self.c).astype(np.int32)
+        self.dev_ct = torch.empty(self.ctable.shape, dtype=torch.int32, device=DEV)
+        self.dev_cc = torch.empty(w.batch, dtype=torch.int32, device=DEV)
+        self.dev_et = torch.empty(self.etable.shape, dtype=torch.int32, device=DEV)
+        self.dev_ec = torch.empty(w.batch, dtype=torch.int32, device=DEV)
+        pkv.page_table_write(self.pool, self.ctable, self.cctx, self.dev_ct, self.dev_cc)
+        pkv.page_table_write(case.pool, self.etable, self.ectx, self.dev_et, self.dev_ec)
+        torch.cuda.synchronize()
+
+    def slots(self, tile, etile=None):
+        etile = etile or tile
+        return (max(1, -(-int(self.cctx.max()) // tile)), max(1, -(-int(self.ectx.max()) // etile)))
+
+    def decode(self, layer, tile, split=0, etile=None, esplit=None):
+        """Compact run with (tile, split), exact run with (etile, esplit),
+        defaulting to the same; one merge over both runs' slots."""
+        w, case = self.w, self.case
+        etile = etile or tile
+        esplit = split if esplit is None else esplit
+        Sc, Se = self.slots(tile, etile)
+        B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+        po = torch.full((B, Hq, Sc + Se, D), float("nan"), device=DEV)
+        pl = torch.full((B, Hq, Sc + Se), float("nan"), device=DEV)
+        o = torch.empty((B, Hq, D), device=DEV)
+        l = torch.empty((B, Hq), device=DEV)
+        nb = max(pkv.decode_workspace_bytes(B, Hq, Sc * tile, tile, D, 0, split),
+                 pkv.decode_workspace_bytes(B, Hq, Se * etile, etile, D, 0, esplit))
+        ws = torch.zeros(max(nb, 16) // 4 + 4, device=DEV)
+        pkv.decode_attention(self.pool, layer, case.q[layer], self.dev_ct, self.dev_cc, 0,
+                             Sc * tile, tile, w.scale, po, pl, workspace=ws, split_tokens=split)
+        pkv.decode_attention(case.pool, layer, case.q[layer], self.dev_et, self.dev_ec, 0,
+                             Se * etile, etile, w.scale, po, pl, workspace=ws, split_tokens=esplit,
+                             slot_offset=Sc)
+        pkv.merge_partials(po, pl, o, l)
+        torch.cuda.synchronize()
+        return po, pl, o, l
+
+    def oracle(self, layer, tile, requests=None, with_exact=True, etile=None):
+        """float64 per request: (partials [Hq, Sc+Se, D], lse [Hq, Sc+Se],
+        out, lse, exact lse, lse bound per head); the last two are None
+        without with_exact."""
+        w = self.w
+        etile = etile or tile
+        Sc, Se = self.slots(tile, etile)
+        qf = self.case.q_f64(layer)
+        grp = w.num_q_heads // w.num_kv_heads
+        res = {}
+        for b in (range(w.batch) if requests is None else requests):
+            kb, vb = kv_bits(self.case, layer, b)
+            c, ctx = int(self.c[b]), w.ctx_lens[b]
+            k2 = np.stack([C.two_runs(kb[g], c) for g in range(w.num_kv_heads)])
+            v2 = np.stack([C.two_runs(vb[g], c) for g in range(w.num_kv_heads)])
+            oc, lc = oracle.tile_partials(qf[b], k2[:, :c], v2[:, :c], w.scale,
+                                          oracle.tile_bounds(c, tile, Sc), w.num_kv_heads)
+            oe, le = oracle.tile_partials(qf[b], k2[:, c:], v2[:, c:], w.scale,
+                                          oracle.tile_bounds(ctx - c, etile, Se), w.num_kv_heads)
+            out, lse = oracle.decode_one_pass(qf[b], k2, v2, ctx, w.scale, w.num_kv_heads)
+            xl = bound = None
+            if with_exact:
+                ke, ve = oracle.widen_bf16(kb), oracle.widen_bf16(vb)
+                _, xl = oracle.decode_one_pass(qf[b], ke, ve, ctx, w.scale, w.num_kv_heads)
+                bound = np.concatenate([
+                    C.lse_error_bound(qf[b][g * grp:(g + 1) * grp], ke[g, :ctx], k2[g, :ctx],
+                                      w.scale) for g in range(w.num_kv_heads)])
+            res[b] = (np.concatenate([oc, oe], axis=1), np.concatenate([lc, le], axis=1),
+                      out, lse, xl, bound)
+        return res
+
+    def check(self, got, ref):
+        po, pl, o, l = [t.cpu().numpy() for t in got]
+        for b, (o_t, l_t, out, lse, xl, bound) in ref.items():
+            assert_out_close(po[b], o_t, what=f"partials b={b}")
+            assert_lse_close(pl[b], l_t, what=f"partial lse b={b}")
+            assert_out_close(o[b], out, what=f"out b={b}")
+            assert_lse_close(l[b], lse, what=f"lse b={b}")
+            # the compact run moves the log-sum-exp by no more than its codes allow
+            if bound is not None and self.w.ctx_lens[b]:
+                assert np.all(np.abs(l[b] - xl) <= bound + LSE_TOL), (b, np.abs(l[b] - xl) - bound)
+
+    def compact_bytes(self):
+        """The compact arena read back: codes [L, P, 2, Hkv, BLOCK] uint8 and
+        scales [L, P, 2, Hkv] float32."""
+        w = self.w
+        P = self.pool.num_pages
+        raw = self.arena.cpu().numpy()
+        nc = w.num_layers * P * 2 * w.num_kv_heads * BLOCK
+        codes = raw[:nc].reshape(w.num_layers, P, 2, w.num_kv_heads, BLOCK)
+        scales = raw[nc:].view(np.float32).reshape(w.num_layers, P, 2, w.num_kv_heads)
+        return codes, scales

@@ -271,15 +271,17 @@ def test_slot_offset_is_checked():
     assert rc == -1 and "num_slots" in msg
 
 
-def test_compact_pools_refuse_append_and_staging():
+def test_compact_pools_refuse_append_and_exact_host_arenas():
     L = pkv.lib()
     cp = FakeCompactPool(8)
     assert L.pkv_append_kv(cp.handle, 0, 1 << 20, 4, 1 << 21, 2, 1 << 22, 1 << 23, None) == -1
     assert "immutable" in err()
+    # a compact staging pool takes a host arena of compact pages (codes and
+    # scales of every layer): an exact-sized host arena is refused
     st = pkv.P()
     rc = L.pkv_stager_create(cp.handle, 1 << 20, pkv.page_bytes(16, 4), 16, 1, 32768, 1,
                              1 << 21, None, None, None, ctypes.byref(st))
-    assert rc == -1 and "exact" in err()
+    assert rc == -1 and "host_bytes" in err()
 
 
 def test_convert_and_crc_arguments_are_refused_on_the_host():

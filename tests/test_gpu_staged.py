@@ -1,8 +1,9 @@
 """Staged tiles from pinned host memory under a lease (pkv_stager_*), on the
 GPU: every window copied in, decoded from the staging buffer and merged
-gives the same bits as the resident decode; an appended tail token flows
-back to the host copy; the lifecycle refuses out-of-order calls and a
-quarantined stager drains before it is released."""
+gives the same bits as the resident decode, for exact and for compact
+pages; an appended tail token flows back to the host copy; the lifecycle
+refuses out-of-order calls and a quarantined stager drains before it is
+released."""
 
 import numpy as np
 import pytest
@@ -10,7 +11,7 @@ import torch
 
 from paged_kv_cache_10_amd import inputs as I
 from paged_kv_cache_10_amd import pkv
-from gpu_helpers import Case, DEV, check_layer, same_bits
+from gpu_helpers import Case, DEV, Runs, check_layer, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -162,3 +163,63 @@ def test_lease_lifecycle_is_enforced(gpu):
     s.seal(c)
     assert s.retire() == 1
     s.destroy()
+
+
+def test_compact_pages_staged_from_host_equal_resident(gpu):
+    """Compact pages (codes and scales) staged window by window from a host
+    copy of a compact pool decode to the same bits as the resident compact
+    pool, at two tilings; a compact stager refuses a tail write-back."""
+    w = workload()
+    table = I.draw_page_tables(w, 3 * WINDOW // 64)
+    case = Case(w, table=table)
+    runs = Runs(case, [n // 64 * 64 for n in w.ctx_lens])      # every full page, scattered ids
+    host = torch.empty(runs.arena.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(runs.arena)
+    wpp, nb = WINDOW // 64, 2
+    cpb = pkv.compact_page_bytes(1, w.num_kv_heads)
+    st_arena = torch.zeros(nb * w.batch * wpp * cpb, dtype=torch.uint8, device=DEV)
+    st_pool = pkv.Pool(st_arena, 1, w.num_kv_heads, compact=True)
+    copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    stager = pkv.Stager(st_pool, host, w.num_layers, w.batch, WINDOW, nb, copy_s, compute, wb_s)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    leases = 0
+    for layer in range(w.num_layers):
+        for tile, split in ((4096, 4096), (8192, 2048)):
+            S = -(-int(runs.cctx.max()) // tile)
+            span = -(-S * tile // WINDOW) * WINDOW
+            res = []
+            for staged in (False, True):
+                po = torch.full((B, Hq, span // tile, D), float("nan"), device=DEV)
+                pl = torch.full((B, Hq, span // tile), float("nan"), device=DEV)
+                nbw = pkv.decode_workspace_bytes(B, Hq, WINDOW if staged else span, tile, D, 0, split)
+                ws = torch.zeros(max(16, nbw) // 4 + 4, device=DEV)
+                if staged:
+                    for begin in range(0, span, WINDOW):
+                        lease = stager.begin(layer, runs.ctable, runs.cctx, begin)
+                        pkv.decode_attention(st_pool, lease.staging_layer, case.q[layer],
+                                             stager.table(lease), runs.dev_cc, begin, WINDOW, tile,
+                                             w.scale, po, pl, workspace=ws, split_tokens=split,
+                                             stream=compute)
+                        stager.seal(lease)
+                        leases += 1
+                else:
+                    pkv.decode_attention(runs.pool, layer, case.q[layer], runs.dev_ct, runs.dev_cc,
+                                         0, span, tile, w.scale, po, pl, workspace=ws,
+                                         split_tokens=split)
+                po, pl = po[:, :, :S].contiguous(), pl[:, :, :S].contiguous()
+                out = torch.empty((B, Hq, D), device=DEV)
+                lse = torch.empty((B, Hq), device=DEV)
+                pkv.merge_partials(po, pl, out, lse)
+                torch.cuda.synchronize()
+                res.append((po, pl, out, lse))
+            for x, y in zip(*res):
+                assert same_bits(x, y), (layer, tile)
+    assert stager.retire() == leases
+    lease = stager.begin(0, runs.ctable, runs.cctx, 0)
+    with pytest.raises(pkv.PkvError) as e:                # compact pages are immutable
+        stager.seal(lease, write_back_tail=True)
+    assert e.value.name == "PKV_ERR_INVALID_ARG"
+    stager.seal(lease)
+    assert stager.retire() == 1
+    stager.destroy()
