@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void convert_kernel(ConvertArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_elem(u, e)));
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  amax = wave_max(amax);
   __shared__ float wmax[4];
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();

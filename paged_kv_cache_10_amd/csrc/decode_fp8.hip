@@ -107,8 +107,7 @@ __device__ __forceinline__ void page_step(uint4 (&kr)[16], uint4 (&vr)[16], f32x
       sc[h * 8 + e] = x;
       cmax = fmaxf(cmax, x);
     }
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  cmax = max_x32(max_x16(cmax));
   const float mn = fmaxf(m, cmax);
   const float mref = (mn == -INFINITY) ? 0.f : mn;
   const float alpha = fast_exp2(m - mref);
@@ -269,8 +268,7 @@ void decode_fp8_kernel(CompactDecodeArgs a) {
     page_step<false>(kr, vr, acc, m, lsum, qrow, cur, a.scale_log2, q, lane, cur);
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = sum_x32(sum_x16(lsum));
   if (q == 0) {
     m_lds[w][n] = m;
     l_lds[w][n] = lsum;

@@ -13,7 +13,8 @@
 //       so that lane l ends up with the scores of tokens 8(l/16) .. +7 of
 //       head l%16, exactly the operand layout PV needs next.
 //   softmax  base-2 running max m and per-lane partial sum l in FP32; the
-//       chunk max meets across the 4 lanes of a head by two xor-shuffles.
+//       chunk max meets across the 4 lanes of a head by two row swaps
+//       (v_permlane16_swap, v_permlane32_swap), with no LDS round trip.
 //   PV  O^T[channel][head] += V^T[16 channels x 32 tokens] . P^T[32 x 16].
 //       V blocks are stored dim-major, so the V^T operand is one contiguous
 //       16-byte load per lane.  P is split as p = hi + lo with hi, lo bf16
@@ -113,8 +114,7 @@ __device__ __forceinline__ void chunk(uint4 (&kr)[2][8], uint4 (&vr)[16], f32x4_
     s[e] = (8 * q + e < live) ? s[e] * scale_log2 : -INFINITY;
     cmax = fmaxf(cmax, s[e]);
   }
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  cmax = max_x32(max_x16(cmax));
   const float mn = fmaxf(m, cmax);
   const float mref = (mn == -INFINITY) ? 0.f : mn;
   const float alpha = fast_exp2(m - mref);
@@ -269,8 +269,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // ---- this wave's (m, l, acc) into LDS
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = sum_x32(sum_x16(lsum));
   if (q == 0) {
     m_lds[w][n] = m;
     l_lds[w][n] = lsum;

@@ -31,18 +31,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
@@ -130,9 +118,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        s[h] += __shfl_xor(s[h], 1);
-        s[h] += __shfl_xor(s[h], 2);
-        s[h] += __shfl_xor(s[h], 4);
+        s[h] = sum8(s[h]);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -189,11 +175,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   for (int r = 0; r < 8; ++r)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float x = acc[r][h];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      acc[r][h] = x;
+      acc[r][h] = sum8(acc[r][h]);
     }
 #pragma unroll
   for (int h = 0; h < G; ++h) {

@@ -58,6 +58,67 @@ __device__ __forceinline__ int rotated_split() {
   return (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
 }
 
+// ---- Wave-level reductions on the VALU's lane-crossing paths, no LDS round
+// trip.  Within a 16-lane row DPP combines lanes (quad_perm [1,0,3,2] pairs
+// lane i with i^1, [2,3,0,1] with i^2, row_half_mirror with the mirror lane
+// of its 8-lane half, row_mirror with the mirror lane of its row);
+// v_permlane16_swap and v_permlane32_swap (gfx950) exchange whole rows, so a
+// value and its swapped copy hold lanes l and l^16 (l^32).  Every step
+// combines two partials over disjoint sets of lanes, and both lanes of a
+// pair compute the same commutative operation, so after the steps up to
+// width w every lane of a w-lane group holds the same bits.
+namespace dpp {
+constexpr int kXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;   // row_half_mirror
+constexpr int kMirror = 0x140;       // row_mirror
+}  // namespace dpp
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+
+// {value of lane l, value of lane l^16} in some order, at every lane l.
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// {value of lane l, value of lane l^32} in some order, at every lane l.
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Over lanes {l, l^16}, {l, l^32}: max and sum.
+__device__ __forceinline__ float max_x16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_x32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_x16(float x) { float a, b; swap16(x, a, b); return a + b; }
+__device__ __forceinline__ float sum_x32(float x) { float a, b; swap32(x, a, b); return a + b; }
+
+// Sum over the 8-lane group of lane l (lanes 8k .. 8k+7).
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_mov<dpp::kXor1>(x);
+  x += dpp_mov<dpp::kXor2>(x);
+  return x + dpp_mov<dpp::kHalfMirror>(x);
+}
+
+// Max and sum over the whole wave.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_mov<dpp::kXor1>(x));
+  x = fmaxf(x, dpp_mov<dpp::kXor2>(x));
+  x = fmaxf(x, dpp_mov<dpp::kHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<dpp::kMirror>(x));
+  return max_x32(max_x16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum8(x);
+  x += dpp_mov<dpp::kMirror>(x);
+  return sum_x32(sum_x16(x));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kMergeThreads = 64;     // one wave; lane i owns channels 128 * half + 2i, +1
 constexpr int kMergeParts = kHeadDim / 128;   // waves per (row, output slot)
-constexpr int kMergeUnroll = 32;      // input slots whose loads are in flight together
+constexpr int kMergeChunk = 64;       // input slots whose loads are in flight together
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int row = blockIdx.x;
@@ -36,10 +36,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const float2* o_in = reinterpret_cast<const float2*>(
       a.in_o + ((int64_t)row * a.in_slots + t0) * kHeadDim + 128 * part) + lane;
 
+  // The output loads of the first 64 slots do not depend on the max: they go
+  // out first, beside this lane's log-sum-exp, so the max and the loads
+  // overlap instead of taking two round trips to memory.
+  float2 o[kMergeChunk];
+  const int n0 = min(kMergeChunk, cnt);
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u)
+    o[u] = (u < n0) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
+  const float lv = (lane < cnt) ? lse_in[lane] : -INFINITY;
+
   // M = max_t lse_t over the group.
-  float m = -INFINITY;
-  for (int t = lane; t < cnt; t += kMergeThreads) m = fmaxf(m, lse_in[t]);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float m = lv;
+  for (int t = lane + kMergeThreads; t < cnt; t += kMergeThreads) m = fmaxf(m, lse_in[t]);
+  m = wave_max(m);
 
   const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
   float2* o_out = reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part) + lane;
@@ -51,30 +61,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 
   // Chunks of 64 slots: lane u computes the weight of the chunk's slot u
   // (one exp per lane, all in parallel), then the slots are summed in
-  // increasing order with each weight read from its lane; the output loads
-  // go out kMergeUnroll at a time ahead of their use.
+  // increasing order with each weight read from its lane.
   float2 acc = make_float2(0.f, 0.f);
   float wsum = 0.f;
-  for (int c0 = 0; c0 < cnt; c0 += kMergeThreads) {
-    const int nc = min(kMergeThreads, cnt - c0);
-    const float wl = (lane < nc) ? expf(lse_in[c0 + lane] - m) : 0.f;   // 0 for an empty slot
+  for (int c0 = 0; c0 < cnt; c0 += kMergeChunk) {
+    const int nc = min(kMergeChunk, cnt - c0);
+    if (c0 > 0) {
 #pragma unroll
-    for (int sb = 0; sb < kMergeThreads / kMergeUnroll; ++sb) {
-      const int t = c0 + sb * kMergeUnroll;
-      const int n = min(kMergeUnroll, cnt - t);
-      if (n <= 0) break;
-      float2 o[kMergeUnroll];
+      for (int u = 0; u < kMergeChunk; ++u)
+        o[u] = (u < nc) ? o_in[(int64_t)(c0 + u) * (kHeadDim / 2)] : make_float2(0.f, 0.f);
+    }
+    const float lt = (c0 == 0) ? lv : ((lane < nc) ? lse_in[c0 + lane] : -INFINITY);
+    const float wl = (lane < nc) ? expf(lt - m) : 0.f;     // 0 for an empty slot
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u)
-        o[u] = (u < n) ? o_in[(int64_t)(t + u) * (kHeadDim / 2)] : make_float2(0.f, 0.f);
-#pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), sb * kMergeUnroll + u));
-        if (w != 0.f) {                        // uniform across the wave
-          acc.x = fmaf(w, o[u].x, acc.x);
-          acc.y = fmaf(w, o[u].y, acc.y);
-          wsum += w;
-        }
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+      if (w != 0.f) {                          // uniform across the wave
+        acc.x = fmaf(w, o[u].x, acc.x);
+        acc.y = fmaf(w, o[u].y, acc.y);
+        wsum += w;
       }
     }
   }
