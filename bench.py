@@ -38,19 +38,20 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "10d0665c375201d9d9dc80d4a5957b45da749f03dbba8fb7ac076ae98afc04da",
+    "source_sha256": "97f22c9132aed0968ffd4322251cd79f144c7f8e8e2cf2b3cc126ac99da6fa00",
     "workload": "long262k", "tile": 4096, "split": 4096,
-    "fetch_kib": 524475.7, "fetch_scale": 1048576 / 524314.1,
-    "write_kib": 1584.05, "write_scale": 1.0,
+    "fetch_kib": 524470.5, "fetch_scale": 1048576 / 524300.1,
+    "write_kib": 1584.0, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/device.h")
 
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "f57d057e001aa057c672433e6da8181252d00d70dd3a2bd970315e88787ba6c0",
-    "fetch_kib": 230026.8, "fetch_scale": 1048576 / 524299.9,
-    "write_kib": 1584.0, "write_scale": 1.0,
+    "source_sha256": "9cf0301f3fe33889797ad6f24cf17a1c1a7ac1abd7e69baeb28971d1d213a1fd",
+    "workload": "long262k", "tile": 4800, "split": 4800,
+    "fetch_kib": 230049.3, "fetch_scale": 1048576 / 524299.9,
+    "write_kib": 1188.0, "write_scale": 1.0,
 }
 FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_amd/csrc/compact.h",
                "paged_kv_cache_10_amd/csrc/device.h")
@@ -86,18 +87,22 @@ def pmc_traffic(workload, tile, split, kernel):
 LAUNCH = {
     "long262k": dict(tile=4096, split=4096),   # 32K windows split-KV 8 ways
     "conc": dict(tile=1984, split=1984),       # 16 full 1,984-token tiles per request
-    "mixed": dict(tile=1728, split=1728),     # 1,020 work-groups: the best measured shape
+    "mixed": dict(tile=3456, split=3456),      # 528 non-empty work-groups: the best measured shape
     "tiny": dict(tile=1024, split=1024),
 }
 
 
 # Runs of two representations (--compact-older): every page older than the
-# newest `exact_tail` tokens is served from compact (E4M3) pages.  The
-# compact run's split gives 256 work-groups at 262K (3,584 tokens x 64
-# splits x 4 KV heads), the exact tail's 512-token splits also 256.  The
-# full-size compact parity test runs exactly these.
+# newest `exact_tail` tokens is served from compact (E4M3) pages.  The two
+# runs are independent until the merge, so the exact tail decodes on a second
+# stream while the compact run decodes, and together they fill the GPU once:
+# the compact run's 4,800-token splits give 192 work-groups at 262K (48
+# splits x 4 KV heads, the last split 3,776 tokens), the exact tail's
+# 2,048-token splits 64 (each work-group reads 2.1-2.5 MB either way).
+# The full-size compact parity test runs exactly these.
 COMPACT_LAUNCH = {
-    "long262k": dict(exact_tail=32768, tile=3584, split=3584, exact_tile=512, exact_split=512),
+    "long262k": dict(exact_tail=32768, tile=4800, split=4800, exact_tile=2048, exact_split=2048,
+                     tail_stream=True),
 }
 
 
@@ -705,42 +710,81 @@ def compact_older(args, w, pool, table, ctx, qs, ref_outs, ref_lses):
              pkv.decode_workspace_bytes(B, Hq, Se * Te, Te, D, 0, Se_))
     ws = torch.zeros(max(16, nb) // 4 + 4, device=dev)
 
-    def step(evs=None):
+    ws2 = torch.zeros_like(ws)          # the tail's own workspace: the runs may overlap
+    side = torch.cuda.Stream() if cl.get("tail_stream") else None
+    forks = [torch.cuda.Event() for _ in range(L)]
+    joins = [torch.cuda.Event() for _ in range(L)]
+
+    def step(evs=None, pair=None, serial=False):
+        """One 16-layer step.  evs: events around each compact launch; pair:
+        events around each layer's two decode runs (fork to join)."""
+        tail = stream if (serial or side is None) else side
         for layer in range(L):
+            if pair is not None:
+                pair[layer][0].record(stream)
+            if tail is not stream:
+                forks[layer].record(stream)
+                tail.wait_event(forks[layer])
+            pkv.decode_attention(pool, layer, qs[layer], det, dec, 0, Se * Te, Te, w.scale,
+                                 po[layer], pl[layer], workspace=ws2, split_tokens=Se_,
+                                 slot_offset=Sc, stream=tail)
+            if tail is not stream:
+                joins[layer].record(tail)
             if evs is not None:
                 evs[layer][0].record(stream)
             pkv.decode_attention(cpool, layer, qs[layer], dct, dcc, 0, Sc * T, T, w.scale,
                                  po[layer], pl[layer], workspace=ws, split_tokens=S, stream=stream)
             if evs is not None:
                 evs[layer][1].record(stream)
-            pkv.decode_attention(pool, layer, qs[layer], det, dec, 0, Se * Te, Te, w.scale,
-                                 po[layer], pl[layer], workspace=ws, split_tokens=Se_,
-                                 slot_offset=Sc, stream=stream)
+            if tail is not stream:
+                stream.wait_event(joins[layer])
+            if pair is not None:
+                pair[layer][1].record(stream)
             pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=stream)
+
+    def timed(**kw):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            step(**kw)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    def event_pass(kind, serial=False):
+        """Mean ms between the two events a step records per layer: kind
+        "evs" brackets the compact launch, "pair" the layer's two runs."""
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(serial=serial, **{kind: ev[k]})
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for evk in ev for (a, b) in evk]))
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+        step(serial=True)
     K = args.steps
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(K):
-        step()
-    t1.record(stream)
+    ms = timed()
+    serial_ms = timed(serial=True)
+    comp_ms = event_pass("evs", serial=True)   # the compact kernel alone on the GPU
+    pair_ms = event_pass("pair")               # both runs of a layer, as timed
+    # one schedule's result must equal the other's bit for bit; the reported
+    # result is the timed schedule's
+    step(serial=True)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / K
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(L)] for _ in range(K)]
-    for k in range(K):
-        step(ev[k])
+    serial_out, serial_lse = outs.clone(), lses.clone()
+    step()
     torch.cuda.synchronize()
-    comp_ms = float(np.mean([a.elapsed_time(b) for evk in ev for (a, b) in evk]))
+    same = bool(torch.equal(outs, serial_out) and torch.equal(lses, serial_lse))
     # the cost of the representation, against the exact path's own result
     d_out = (outs - ref_outs).abs()
     d_lse = (lses - ref_lses).abs()
     t = PMC_TRAFFIC_FP8
     fp8_traffic = None
-    if w.name == "long262k" and sources_sha256(FP8_SOURCES) == t["source_sha256"]:
+    if ((w.name, T, S) == (t["workload"], t["tile"], t["split"])
+            and sources_sha256(FP8_SOURCES) == t["source_sha256"]):
         fp8_traffic = int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
 
     comp_bytes_layer = int(c.sum()) * 2 * Hkv * D + int(npc.sum()) * 2 * Hkv * 4
@@ -757,10 +801,15 @@ def compact_older(args, w, pool, table, ctx, qs, ref_outs, ref_lses):
         "config": {"workload": f"{w.name}: pages older than the newest {cl['exact_tail']} tokens "
                                f"served from compact E4M3 pages (per-block FP32 scale), the tail "
                                f"exact; compact run tile {T} split {S}, exact run tile {Te} "
-                               f"split {Se_}", "compact_tokens": int(c.sum()),
-                   "exact_tokens": int(ectx.sum())},
+                               f"split {Se_}" + (", the tail on a second stream concurrent with "
+                                                 "the compact run" if side is not None else ""),
+                   "compact_tokens": int(c.sum()), "exact_tokens": int(ectx.sum())},
         "tokens_per_s": round(B / (ms * 1e-3), 2),
         "bytes_moved_per_step": moved,
+        "moved_GBs": round(moved / (ms * 1e-3) / 1e9, 1),
+        "serial_ms_per_step": round(serial_ms, 4),
+        "decode_runs_ms_per_layer": round(pair_ms, 5),
+        "schedules_bitwise_equal": same,
         "bytes_per_token_layer": {"exact": 2 * Hkv * D * 2,
                                   "compact": round(comp_bytes_layer / max(1, int(c.sum())), 3)},
         "vs_exact_path": {"max_abs_out": round(float(d_out.max()), 5),

@@ -218,9 +218,11 @@ class Runs:
         etile = etile or tile
         return (max(1, -(-int(self.cctx.max()) // tile)), max(1, -(-int(self.ectx.max()) // etile)))
 
-    def decode(self, layer, tile, split=0, etile=None, esplit=None):
+    def decode(self, layer, tile, split=0, etile=None, esplit=None, tail_stream=False):
         """Compact run with (tile, split), exact run with (etile, esplit),
-        defaulting to the same; one merge over both runs' slots."""
+        defaulting to the same; one merge over both runs' slots.  With
+        tail_stream the exact run decodes on a second stream, concurrent
+        with the compact run, and is joined before the merge."""
         w, case = self.w, self.case
         etile = etile or tile
         esplit = split if esplit is None else esplit
@@ -233,12 +235,20 @@ class Runs:
         nb = max(pkv.decode_workspace_bytes(B, Hq, Sc * tile, tile, D, 0, split),
                  pkv.decode_workspace_bytes(B, Hq, Se * etile, etile, D, 0, esplit))
         ws = torch.zeros(max(nb, 16) // 4 + 4, device=DEV)
-        pkv.decode_attention(self.pool, layer, case.q[layer], self.dev_ct, self.dev_cc, 0,
-                             Sc * tile, tile, w.scale, po, pl, workspace=ws, split_tokens=split)
+        ws_tail = torch.zeros_like(ws)
+        main = torch.cuda.current_stream()
+        tail = torch.cuda.Stream() if tail_stream else main
+        if tail_stream:
+            tail.wait_stream(main)
         pkv.decode_attention(case.pool, layer, case.q[layer], self.dev_et, self.dev_ec, 0,
-                             Se * etile, etile, w.scale, po, pl, workspace=ws, split_tokens=esplit,
-                             slot_offset=Sc)
-        pkv.merge_partials(po, pl, o, l)
+                             Se * etile, etile, w.scale, po, pl, workspace=ws_tail,
+                             split_tokens=esplit, slot_offset=Sc, stream=tail)
+        pkv.decode_attention(self.pool, layer, case.q[layer], self.dev_ct, self.dev_cc, 0,
+                             Sc * tile, tile, w.scale, po, pl, workspace=ws, split_tokens=split,
+                             stream=main)
+        if tail_stream:
+            main.wait_stream(tail)
+        pkv.merge_partials(po, pl, o, l, stream=main)
         torch.cuda.synchronize()
         return po, pl, o, l
 

@@ -222,6 +222,12 @@ def long_runs():
 def test_long262k_two_runs_match_oracle(gpu, long_runs, layer):
     from bench import COMPACT_LAUNCH
     cl = COMPACT_LAUNCH["long262k"]
-    got = long_runs.decode(layer, cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"])
+    got = long_runs.decode(layer, cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"],
+                           tail_stream=cl["tail_stream"])
     long_runs.check(got, long_runs.oracle(layer, cl["tile"], with_exact=False,
                                           etile=cl["exact_tile"]))
+    # the runs write disjoint slots: decoding them one after the other on one
+    # stream gives the same bits
+    serial = long_runs.decode(layer, cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"])
+    for a, b in zip(got, serial):
+        assert torch.equal(a, b)
