@@ -38,9 +38,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "97f22c9132aed0968ffd4322251cd79f144c7f8e8e2cf2b3cc126ac99da6fa00",
+    "source_sha256": "a6ab12cdac72b3b96d106670443b2eddf19dcd0671c14a4073ee30d925ec0ed9",
     "workload": "long262k", "tile": 4096, "split": 4096,
-    "fetch_kib": 524470.5, "fetch_scale": 1048576 / 524300.1,
+    "fetch_kib": 524500.0, "fetch_scale": 1048576 / 524300.1,
     "write_kib": 1584.0, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/device.h")
@@ -48,9 +48,9 @@ KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "9cf0301f3fe33889797ad6f24cf17a1c1a7ac1abd7e69baeb28971d1d213a1fd",
+    "source_sha256": "586625b1c72ab107813b1d5389c45267457b6176be439aff689484ee46c9bb9a",
     "workload": "long262k", "tile": 4800, "split": 4800,
-    "fetch_kib": 230049.3, "fetch_scale": 1048576 / 524299.9,
+    "fetch_kib": 230090.7, "fetch_scale": 1048576 / 524299.9,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_amd/csrc/compact.h",
@@ -86,8 +86,10 @@ def pmc_traffic(workload, tile, split, kernel):
 # layers are independent), and the line reports the other schedule as well.
 LAUNCH = {
     "long262k": dict(tile=4096, split=4096),   # 32K windows split-KV 8 ways
-    "conc": dict(tile=1984, split=1984),       # 16 full 1,984-token tiles per request
-    "mixed": dict(tile=3456, split=3456),      # 528 non-empty work-groups: the best measured shape
+    "conc": dict(tile=8192, split=2048),       # the workload's 8,192-token tiles, split-KV 4 ways
+    # per-request tiles planned for 256 work-groups (one per CU); --plan 0
+    # runs the fixed 4,096-token tiling instead
+    "mixed": dict(tile=4096, split=4096, plan=256),
     "tiny": dict(tile=1024, split=1024),
 }
 
@@ -115,6 +117,9 @@ def parse():
     ap.add_argument("--tile", type=int, default=0, help="tile tokens (default: LAUNCH)")
     ap.add_argument("--split", type=int, default=0, help="tokens per work-group (default: LAUNCH)")
     ap.add_argument("--kernel", default="mfma", choices=["mfma", "valu"])
+    ap.add_argument("--plan", type=int, default=None,
+                    help="per-request tiles planned for this many work-groups (0: the fixed "
+                         "tiling; default: LAUNCH)")
     ap.add_argument("--staged", action="store_true",
                     help="decode each 32,768-token staging window with its own call")
     ap.add_argument("--serial", action="store_true",
@@ -161,6 +166,11 @@ def main():
 
     w = I.workload(args.workload)
     launch = LAUNCH.get(args.workload, {})
+    # per-request tiles (LAUNCH "plan"): only where nothing asks for the fixed tiling
+    plan = launch.get("plan", 0) if args.plan is None else args.plan
+    if (args.tile or args.split or args.staged or args.kernel != "mfma" or args.host_staged
+            or args.compact_older):
+        plan = 0
     w.tile_tokens = args.tile or launch.get("tile", w.tile_tokens)
     args.split = args.split or launch.get("split", 0)
     overlap = args.overlap and not args.serial
@@ -169,8 +179,14 @@ def main():
 
     # ---------------------------------------------------------------- inputs
     t_gen = time.time()
-    slots = -(-w.max_ctx // T)
-    span = slots * T
+    if plan:
+        row_tiles, max_tiles = pkv.plan_tiles(w.ctx_lens, Hkv, plan)
+        max_row = int(row_tiles.max())
+        slots = max_tiles
+        span = max_tiles * max_row
+    else:
+        slots = -(-w.max_ctx // T)
+        span = slots * T
     width = span // w.page_tokens
     table = I.draw_page_tables(w, width)
     ctx = np.array(w.ctx_lens, dtype=np.int32)
@@ -187,6 +203,7 @@ def main():
             k, v = I.device_kv(w, layer, b, dev)
             I.device_scatter(arena, w, layer, b, table[b], k, v)
             del k, v
+    d_rt = torch.from_numpy(row_tiles).to(dev) if plan else None
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
@@ -204,15 +221,22 @@ def main():
     decoded = [torch.cuda.Event() for _ in range(L)]
     merged = torch.cuda.Event()
 
+    def decode_layer(layer):
+        if plan:
+            pkv.decode_attention_rows(pool, layer, qs[layer], dt, dc, d_rt, max_row, max_tiles,
+                                      w.scale, po[layer], pl[layer], stream=stream)
+            return
+        for begin in range(0, span, window):
+            pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc,
+                                 begin, min(window, span - begin), T, w.scale, po[layer],
+                                 pl[layer], workspace=ws, kernel=args.kernel,
+                                 split_tokens=args.split, stream=stream)
+
     def step(evs=None, overlap=overlap):
         for layer in range(L):
             if evs is not None:
                 evs[layer][0].record(stream)
-            for begin in range(0, span, window):
-                pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc,
-                                     begin, min(window, span - begin), T, w.scale, po[layer],
-                                     pl[layer], workspace=ws, kernel=args.kernel,
-                                     split_tokens=args.split, stream=stream)
+            decode_layer(layer)
             if evs is not None:
                 evs[layer][1].record(stream)
             if overlap:
@@ -271,11 +295,7 @@ def main():
     ref_o, ref_l = outs.clone(), lses.clone()
     for layer in range(L):
         po[layer].fill_(float("nan"))
-        for begin in range(0, span, window):
-            pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc, begin,
-                                 min(window, span - begin), T, w.scale, po[layer], pl[layer],
-                                 workspace=ws, kernel=args.kernel, split_tokens=args.split,
-                                 stream=stream)
+        decode_layer(layer)
         pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=stream)
     torch.cuda.synchronize()
     self_check = bool(torch.equal(ref_o.view(torch.int32), outs.view(torch.int32))
@@ -321,9 +341,12 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {B} x {w.max_ctx if B == 1 else 'mixed'} tokens, {L} layers, "
-                        f"{Hq} q / {Hkv} kv heads, head_dim {D}, 64-token pages, tile {T}"
+                        f"{Hq} q / {Hkv} kv heads, head_dim {D}, 64-token pages, "
+                        + (f"per-request tiles planned for {plan} work-groups (at most "
+                           f"{max_row} tokens, {max_tiles} per request)" if plan else f"tile {T}")
                         + (", staged 32768-token windows" if args.staged else ""),
-            "batch": B, "ctx_lens_sum": int(sum(w.ctx_lens)), "layers": L, "tile_tokens": T,
+            "batch": B, "ctx_lens_sum": int(sum(w.ctx_lens)), "layers": L,
+            "tile_tokens": row_tiles.tolist() if plan else T,
             "kernel": args.kernel, "split_tokens": args.split or "default",
             "merge_overlapped": overlap,
             "parallelism": "none (1 GPU)",
@@ -331,22 +354,24 @@ def main():
         "tokens_per_s": round(tok_s, 2),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv_bytes_step,
-        "total_bytes_per_step": total_bytes_step(w, T, ws_bytes > 0),
+        "total_bytes_per_step": total_bytes_step(
+            w, slots, ws_bytes // (B * Hq * (D + 1) * 4) * (span // window)),
         "passes": {"n": len(passes), "ms_per_step_median": round(float(np.median(passes)), 4),
                    "ms_per_step_min": round(min(passes), 4),
                    "ms_per_step_max": round(max(passes), 4)},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_mfma_kernel" if args.kernel == "mfma" else "decode_valu_kernel",
-            "launch": "one pkv_decode_attention call per layer = the decode kernel"
-                      + ("" if ws_bytes == 0 else " + the tile finalize"),
+            "launch": ("one pkv_decode_attention_rows call per layer = the decode kernel" if plan
+                       else "one pkv_decode_attention call per layer = the decode kernel"
+                       + ("" if ws_bytes == 0 else " + the tile finalize")),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_ms": round(dec_avg_ms, 5),
-            "traffic": pmc_traffic(args.workload, T, args.split, args.kernel),
+            "traffic": None if plan else pmc_traffic(args.workload, T, args.split, args.kernel),
         },
         "setup_s": round(t_gen, 1),
         "overlapped_equals_serial_bitwise": self_check,
@@ -551,22 +576,21 @@ def merge_stress(args, ceiling):
     return res
 
 
-def total_bytes_step(w, T, finalize):
+def total_bytes_step(w, slots, split_slots=0):
     """Every byte one step moves, not only KV: per layer the KV history, q,
-    the page-table entries read, the tile partials written (and, where a
-    tile has several splits, the split partials written and read back), the
-    partials read by the merge, and out and lse written."""
+    the page-table entries read, the tile partials written (slots per row;
+    and, where a tile has several splits, the split_slots split partials
+    written and read back), the partials read by the merge, and out and lse
+    written."""
     PT = w.page_tokens
     rows = w.batch * w.num_q_heads
-    slots = -(-w.max_ctx // T)
     pages = sum(-(-c // PT) for c in w.ctx_lens)
     per_layer = (w.kv_bytes_per_step // w.num_layers
                  + rows * w.head_dim * 2                        # q (bf16)
                  + pages * 4                                    # page-table entries
                  + 2 * rows * slots * (w.head_dim + 1) * 4      # partials written, then read
                  + rows * (w.head_dim + 1) * 4)                 # out + lse
-    if finalize:
-        per_layer += 2 * rows * slots * (w.head_dim + 1) * 4    # split partials, written and read
+    per_layer += 2 * rows * split_slots * (w.head_dim + 1) * 4  # split partials, written and read
     return per_layer * w.num_layers
 
 

@@ -82,7 +82,7 @@ typedef struct pkv_pool pkv_pool;   /* opaque host-side handle */
 const char* pkv_last_error(void);
 
 /* Library ABI version (PKV_ABI_VERSION). */
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 int32_t pkv_abi_version(void);
 
 /* Bytes of one physical page (all layers) for `geom`. */
@@ -244,6 +244,48 @@ int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
                          void* workspace, uint64_t workspace_bytes,
                          const pkv_decode_opts* opts, void* stream);
 
+/* ------------------------------------------------ per-request tiles --
+ * Tiles of their own length for each request of a batch (the same per-tile
+ * partials and merge as above; the KV-cache engineering page, section
+ * "Exact recent pages, compact older pages", leaves the tile length free).
+ * A batch of very different lengths cut into one tile length leaves most
+ * work-groups short or idle; planning each request's tiles so that every
+ * work-group of the launch carries about the same number of tokens fills
+ * the GPU evenly.  The plan depends on all the batch's lengths, so a
+ * request's partials (not its merged result, up to rounding) depend on the
+ * batch: use the fixed tiling above where bit-identity across batches or
+ * staged windows matters.
+ *
+ * pkv_plan_tiles (host only): tau = the smallest multiple of 64 up to
+ * max_tile_tokens for which num_kv_heads * sum_b ceil(ctx_b / tau) <=
+ * work_groups (max_tile_tokens if none); request b is cut into n_b =
+ * ceil(ctx_b / tau) tiles of host_row_tile_tokens[b] = ctx_b / n_b rounded
+ * up to a multiple of 64 (64 for an empty request); *max_tiles_out =
+ * max(1, max_b n_b).  Deterministic.
+ *   host_ctx_lens [batch] >= 0; work_groups >= 1 (256 = one per CU on
+ *   MI355X); max_tile_tokens a multiple of 64 in 64..16384.
+ *
+ * pkv_decode_attention_rows: tile t of request b covers tokens
+ * [t T_b, min((t+1) T_b, ctx_b)) with T_b = dev_row_tile_tokens[b]; tiles
+ * 0 .. max_tiles-1 of every row are written to slots opts.slot_offset + t
+ * (out = 0, lse = -inf for a tile past ctx_b).  max_row_tile_tokens >=
+ * every T_b (the plan's maximum); pt_stride >= max_tiles *
+ * max_row_tile_tokens / 64.  MFMA kernel and bf16 pools only
+ * (opts.kernel 0 or 2, opts.split_tokens 0); no workspace (each tile is one
+ * work-group).  A device T_b that is not a multiple of 64 in 64..16384, or
+ * a request longer than max_tiles * T_b, is not silently cut: the affected
+ * row's partial carries lse = NaN (the host cannot read device lengths
+ * without a sync).  Other arguments as pkv_decode_attention. */
+int pkv_plan_tiles(const int32_t* host_ctx_lens, int32_t batch, int32_t num_kv_heads,
+                   int32_t work_groups, int32_t max_tile_tokens, int32_t* host_row_tile_tokens,
+                   int32_t* max_tiles_out);
+int pkv_decode_attention_rows(const pkv_pool* pool, int32_t layer, const void* q,
+                              const int32_t* dev_table, int32_t pt_stride,
+                              const int32_t* dev_ctx_lens, int32_t batch, int32_t num_q_heads,
+                              const int32_t* dev_row_tile_tokens, int32_t max_row_tile_tokens,
+                              int32_t max_tiles, float scale, float* part_out, float* part_lse,
+                              int32_t num_slots, const pkv_decode_opts* opts, void* stream);
+
 /* --------------------------------------------------------------- merge --
  * FP32 log-sum-exp merge of the partials of each row (KV-cache engineering
  * page, section "Exact recent pages, compact older pages").  For row r,
@@ -254,6 +296,7 @@ int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
  * Slots with lse = -inf add nothing (their part_out is never read into the
  * sums), and the sums run over t in increasing order, so inserting empty
  * slots leaves the result bit-identical and a single slot merges to itself.
+ * A slot with lse = NaN (a flagged partial) makes its row's out and lse NaN.
  *   part_out [rows][num_slots][head_dim], part_lse [rows][num_slots] (rows =
  *   batch * num_q_heads), out [rows][head_dim], lse [rows]; all FP32 device.
  * head_dim must be 256.  num_slots >= 1. */

@@ -402,6 +402,7 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
   a.token_begin = token_begin;
   a.token_count = token_count;
   a.split_tokens = split;
+  a.row_split = nullptr;
   a.scale_log2 = scale * pkv::kLog2e;
 
   const int n_split = token_count / split;
@@ -464,6 +465,120 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
     if (e != hipSuccess)
       return fail(PKV_ERR_LAUNCH, "tile finalize launch failed: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+PKV_API int pkv_plan_tiles(const int32_t* host_ctx_lens, int32_t batch, int32_t num_kv_heads,
+                           int32_t work_groups, int32_t max_tile_tokens,
+                           int32_t* host_row_tile_tokens, int32_t* max_tiles_out) {
+  if (batch < 0 || batch > 65535) return fail(PKV_ERR_INVALID_ARG, "batch = %d outside 0..65535", batch);
+  if (num_kv_heads < 1) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads = %d, need >= 1", num_kv_heads);
+  if (work_groups < 1) return fail(PKV_ERR_INVALID_ARG, "work_groups = %d, need >= 1", work_groups);
+  if (max_tile_tokens < pkv::kPageTokens || max_tile_tokens > kMaxMfmaSplit ||
+      max_tile_tokens % pkv::kPageTokens)
+    return fail(PKV_ERR_INVALID_ARG, "max_tile_tokens = %d must be a multiple of %d in %d..%d",
+                max_tile_tokens, pkv::kPageTokens, pkv::kPageTokens, kMaxMfmaSplit);
+  if (!max_tiles_out || (batch > 0 && (!host_ctx_lens || !host_row_tile_tokens)))
+    return fail(PKV_ERR_INVALID_ARG, "host_ctx_lens, host_row_tile_tokens or max_tiles_out is NULL");
+  for (int b = 0; b < batch; ++b)
+    if (host_ctx_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "ctx_lens[%d] = %d is negative", b, host_ctx_lens[b]);
+  const int PT = pkv::kPageTokens;
+  // work-groups with every split at most tau tokens
+  auto groups = [&](int64_t tau) {
+    int64_t n = 0;
+    for (int b = 0; b < batch; ++b) n += (host_ctx_lens[b] + tau - 1) / tau;
+    return n * num_kv_heads;
+  };
+  // smallest multiple of 64 (up to the maximum) whose split count fits
+  int lo = 1, hi = max_tile_tokens / PT;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (groups((int64_t)mid * PT) <= work_groups) hi = mid;
+    else lo = mid + 1;
+  }
+  const int64_t tau = (int64_t)lo * PT;
+  int max_tiles = 1;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t c = host_ctx_lens[b];
+    const int64_t n = (c + tau - 1) / tau;                    // splits of this request
+    const int64_t even = n > 0 ? (c + n - 1) / n : PT;         // equal shares of its tokens
+    host_row_tile_tokens[b] = (int32_t)((even + PT - 1) / PT * PT);
+    if (n > max_tiles) max_tiles = (int)n;
+  }
+  *max_tiles_out = max_tiles;
+  return ok();
+}
+
+PKV_API int pkv_decode_attention_rows(const pkv_pool* pool, int32_t layer, const void* q,
+                                      const int32_t* dev_table, int32_t pt_stride,
+                                      const int32_t* dev_ctx_lens, int32_t batch,
+                                      int32_t num_q_heads, const int32_t* dev_row_tile_tokens,
+                                      int32_t max_row_tile_tokens, int32_t max_tiles, float scale,
+                                      float* part_out, float* part_lse, int32_t num_slots,
+                                      const pkv_decode_opts* opts, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  const pkv_geom& G = pool->geom;
+  if (layer < 0 || layer >= G.num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer = %d outside 0..%d", layer, G.num_layers - 1);
+  if (batch < 0 || batch > 65535) return fail(PKV_ERR_INVALID_ARG, "batch = %d outside 0..65535", batch);
+  if (num_q_heads < 1 || num_q_heads % G.num_kv_heads)
+    return fail(PKV_ERR_GEOMETRY, "num_q_heads = %d must be a positive multiple of num_kv_heads = %d",
+                num_q_heads, G.num_kv_heads);
+  const int group = num_q_heads / G.num_kv_heads;
+  int kernel = 0;
+  if (int rc = kernel_for(opts, group, &kernel)) return rc;
+  if (kernel != 2 || pool->format != PKV_FORMAT_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "per-request tiles are decoded by the MFMA kernel from bf16 pools only");
+  if (opts && opts->split_tokens != 0)
+    return fail(PKV_ERR_INVALID_ARG, "opts.split_tokens = %d: per-request tiles are their own splits",
+                opts->split_tokens);
+  if (max_row_tile_tokens < G.page_tokens || max_row_tile_tokens > kMaxMfmaSplit ||
+      max_row_tile_tokens % G.page_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "max_row_tile_tokens = %d must be a multiple of %d in %d..%d",
+                max_row_tile_tokens, G.page_tokens, G.page_tokens, kMaxMfmaSplit);
+  if (max_tiles < 1 || max_tiles > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "max_tiles = %d outside 1..65535", max_tiles);
+  const int64_t span = (int64_t)max_tiles * max_row_tile_tokens;
+  if (span > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "max_tiles x max_row_tile_tokens overflows int32");
+  if ((int64_t)pt_stride * G.page_tokens < span)
+    return fail(PKV_ERR_INVALID_ARG, "pt_stride = %d covers %lld tokens, less than max_tiles x "
+                "max_row_tile_tokens = %lld", pt_stride, (long long)pt_stride * G.page_tokens,
+                (long long)span);
+  const int slot_offset = opts ? opts->slot_offset : 0;
+  if (slot_offset < 0) return fail(PKV_ERR_INVALID_ARG, "opts.slot_offset = %d is negative", slot_offset);
+  if (num_slots < 1 || num_slots > 65535 || (int64_t)slot_offset + max_tiles > num_slots)
+    return fail(PKV_ERR_INVALID_ARG, "slots %d..%d exceed num_slots = %d", slot_offset,
+                slot_offset + max_tiles - 1, num_slots);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (batch == 0) return ok();
+  if (!q || !dev_table || !dev_ctx_lens || !dev_row_tile_tokens || !part_out || !part_lse)
+    return fail(PKV_ERR_INVALID_ARG,
+                "q, dev_table, dev_ctx_lens, dev_row_tile_tokens, part_out or part_lse is NULL");
+  if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(part_out) % 16)
+    return fail(PKV_ERR_INVALID_ARG, "q and part_out must be 16-byte aligned");
+
+  pkv::DecodeArgs a;
+  a.arena = static_cast<const uint16_t*>(pool->base);
+  a.page_elems = (int64_t)(pool->page_layer_bytes / 2);
+  a.layer_off = (int64_t)(pool->page_layer_bytes / 2) * pool->num_pages * layer;
+  a.num_pages = (int32_t)pool->num_pages;
+  a.num_kv_heads = G.num_kv_heads;
+  a.q = static_cast<const uint16_t*>(q);
+  a.table = dev_table;
+  a.pt_stride = pt_stride;
+  a.ctx_lens = dev_ctx_lens;
+  a.num_q_heads = num_q_heads;
+  a.token_begin = 0;                   // the window: every row's max_tiles splits
+  a.token_count = (int32_t)span;
+  a.split_tokens = max_row_tile_tokens;   // sets the grid row: token_count / split_tokens
+  a.row_split = dev_row_tile_tokens;
+  a.scale_log2 = scale * pkv::kLog2e;
+  a.out_o = part_out;
+  a.out_lse = part_lse;
+  a.out_slots = num_slots;
+  a.out_slot0 = slot_offset;
+  hipError_t e = pkv::launch_decode_mfma(a, batch, group, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -164,9 +164,10 @@ void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
-  const int split = rotated_split();
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  const WorkItem item = dense_item(a.ctx_lens, a.row_split, a.token_begin, a.token_count, a.split_tokens);
+  const int split = item.split;
+  const int g = item.g;
+  const int b = item.b;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
@@ -174,16 +175,34 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int q = lane >> 4;        // k-group of operands / row group of results
 
   const int win_end = a.token_begin + a.token_count;
-  const int ctx = max(0, min(a.ctx_lens[b], win_end));
-  const int t0 = a.token_begin + split * a.split_tokens;
-  const int t1 = min(t0 + a.split_tokens, ctx);
+  const int ctx = max(0, min(item.ctx, win_end));
+  const int S = item.S;
+  const int t0 = a.token_begin + split * S;
+  const int t1 = min(t0 + S, ctx);
   const int slot = a.out_slot0 + split;
+  // per-request splits: keys past the grid row's last split (a split too
+  // short for the row's slots) are not attended, and that row's last
+  // partial says so with a NaN log-sum-exp
+  const bool uncovered = a.row_split && split == (int)gridDim.x - 1 &&
+                         item.ctx > a.token_begin + (split + 1) * S;
   const int64_t row0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[16 * kQPad];
   __shared__ float acc_lds[kWaves][G][D];
   __shared__ float m_lds[kWaves][16];
   __shared__ float l_lds[kWaves][16];
+
+  // ---- a malformed per-request split (outside 64 .. 16,384 tokens or not a
+  // multiple of 64): nothing is read, and the partial says so with a NaN
+  // log-sum-exp
+  if (a.row_split && (S < PT || S > 64 * kWaves * PT || S % PT != 0)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      a.out_o[((row0 + h) * a.out_slots + slot) * D + tid] = 0.f;
+      if (tid == 0) a.out_lse[(row0 + h) * a.out_slots + slot] = NAN;
+    }
+    return;
+  }
 
   // ---- a split with no key of the request: an empty partial, nothing read
   if (t1 <= t0) {
@@ -302,7 +321,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     const bool live = L > 0.f;
     a.out_o[((row0 + h) * a.out_slots + slot) * D + tid] = live ? o / L : 0.f;
     if (tid == 0)
-      a.out_lse[(row0 + h) * a.out_slots + slot] = live ? (M + log2f(L)) * kLn2 : -INFINITY;
+      a.out_lse[(row0 + h) * a.out_slots + slot] =
+          uncovered ? NAN : (live ? (M + log2f(L)) * kLn2 : -INFINITY);
   }
 }
 

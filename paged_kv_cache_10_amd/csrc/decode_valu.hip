@@ -36,9 +36,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
-  const int split = rotated_split();
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  const WorkItem item = dense_item(a.ctx_lens, nullptr, a.token_begin, a.token_count, a.split_tokens);
+  const int split = item.split;
+  const int g = item.g;
+  const int b = item.b;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int tg = lane >> 3;    // token within an 8-token step (QK) / channel row (PV)
 
   const int win_end = a.token_begin + a.token_count;
-  const int ctx = max(0, min(a.ctx_lens[b], win_end));
+  const int ctx = max(0, min(item.ctx, win_end));
   const int t0 = a.token_begin + split * a.split_tokens;
   const int t1 = min(t0 + a.split_tokens, ctx);
   const int slot = a.out_slot0 + split;

@@ -46,16 +46,133 @@ __device__ __forceinline__ int v_piece(int d, int u) {
   return ((u >> 2) * 16 + (d >> 4)) * 64 + (u & 3) * 16 + (d & 15);
 }
 
-// XCD-aware placement.  Work-groups are dealt to the 8 XCDs round-robin by
-// linear id, and every (request, KV head) row of the grid starts at split 0,
-// which is often the row's only non-empty split; with a row length that is a
-// multiple of 8 every row's split 0 would land on one XCD.  Rotating each
-// row's splits by a row-dependent amount spreads them; a split's arithmetic
-// does not depend on which work-group runs it.
-__device__ __forceinline__ int rotated_split() {
-  const unsigned row = blockIdx.y + gridDim.y * blockIdx.z;
-  const unsigned rot = (row & 7u) % gridDim.x;
-  return (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
+// Work order of a decode launch.  The grid holds one work-group per (split,
+// KV head, request): gridDim = (splits per row, KV heads, requests).  The
+// hardware deals work-groups to the 8 XCDs round-robin by linear id and
+// starts them in that order, so the linear id decides where and when a split
+// runs.  The order used: every non-empty split first, request by request, KV
+// head by KV head, split by split; then the empty splits (those wholly past a
+// request's length) in the same order.  Consecutive splits of a row so land
+// on consecutive XCDs, the real work starts in the first rounds on all CUs,
+// and the empty work-groups (which only write an empty partial) run last,
+// in the gaps the finishing work leaves.  Within a row the live splits are
+// rotated by (row mod 8), so the KV heads of one split, which read the same
+// pages, start on different XCDs (measured: ~1 % faster than leaving them
+// on one).  A split's arithmetic does not depend on which work-group runs
+// it, so the order changes no result bit.
+struct WorkItem {
+  int b;       // request
+  int g;       // KV head
+  int split;   // split within the window
+  int ctx;     // ctx_lens[b]
+  int S;       // tokens per split of request b
+};
+
+// Splits of request b's row that hold at least one key of the window.
+__device__ __forceinline__ int live_splits(int ctx, int token_begin, int token_count,
+                                           int split_tokens) {
+  const int c = min(ctx, token_begin + token_count) - token_begin;
+  return c > 0 ? (c + split_tokens - 1) / split_tokens : 0;
+}
+
+// The item at position j of request b's items in a pass (0: its ph = live
+// live splits per KV head, 1: its ph empty splits per KV head).
+__device__ __forceinline__ WorkItem item_at(int b, unsigned j, unsigned ph, unsigned live,
+                                            int pass, unsigned hkv, int ctx, int S) {
+  WorkItem it;
+  it.b = b;
+  const unsigned g = j / ph;
+  const unsigned pos = j - g * ph;
+  it.g = (int)g;
+  if (pass == 0) {
+    // a row's live splits rotated by (row mod 8): the KV heads of one split
+    // (the same pages) then start on different XCDs
+    unsigned rot = (g + hkv * (unsigned)b) & 7u;
+    if (rot >= ph) rot %= ph;
+    const unsigned r = pos + ph - rot;            // < 2 ph
+    it.split = (int)(r >= ph ? r - ph : r);
+  } else {
+    it.split = (int)(live + pos);
+  }
+  it.ctx = ctx;
+  it.S = S;
+  return it;
+}
+
+// This work-group's item.  Up to 4 requests the lengths are read with
+// uniform (scalar) loads and walked in order; beyond, every wave computes the
+// item in parallel (the same value): lane j holds request 64k + j of chunk
+// k, and an exclusive prefix over the chunk's lanes (readlane broadcasts,
+// uniform) locates the request whose items contain the linear id.
+// row_split (or null) gives each request its own split length; a request
+// needing more splits than the grid row holds gets the row's splits (the
+// kernel flags the uncovered rest).
+__device__ __forceinline__ WorkItem dense_item(const int32_t* ctx_lens, const int32_t* row_split,
+                                               int token_begin, int token_count,
+                                               int split_tokens) {
+  // grid sizes and ids are uniform: readfirstlane keeps the walk below
+  // (and its loads) on the scalar unit
+  const unsigned n_split = __builtin_amdgcn_readfirstlane(gridDim.x);
+  const unsigned hkv = __builtin_amdgcn_readfirstlane(gridDim.y);
+  const int batch = __builtin_amdgcn_readfirstlane(gridDim.z);
+  const unsigned lin = blockIdx.x + n_split * (blockIdx.y + hkv * blockIdx.z);
+  // live splits of a request; a malformed per-request split reads nothing
+  auto live_of = [&](int ctx, int S) {
+    return S >= kPageTokens ? min(live_splits(ctx, token_begin, token_count, S), (int)n_split) : 0;
+  };
+  if (batch <= 4) {
+    int cs[4], ss[4], lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {            // every load issued before any is used
+      cs[i] = (i < batch) ? ctx_lens[i] : 0;
+      ss[i] = (i < batch) ? (row_split ? row_split[i] : split_tokens) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lv[i] = (i < batch) ? live_of(cs[i], ss[i]) : 0;
+    unsigned base = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= batch) break;
+        const unsigned ph = pass == 0 ? (unsigned)lv[i] : n_split - (unsigned)lv[i];
+        const unsigned v = ph * hkv;
+        if (lin < base + v) return item_at(i, lin - base, ph, lv[i], pass, hkv, cs[i], ss[i]);
+        base += v;
+      }
+    }
+  } else {
+    const int lane = threadIdx.x & 63;
+    unsigned base = 0;                       // items of this pass before the chunk
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int c0 = 0; c0 < batch; c0 += 64) {
+        const int b = c0 + lane;
+        const int cb = (b < batch) ? ctx_lens[b] : 0;
+        const int sb = (b < batch) ? (row_split ? row_split[b] : split_tokens) : 0;
+        const int live = (b < batch) ? live_of(cb, sb) : 0;
+        const unsigned per_head = (b < batch) ? (pass == 0 ? live : n_split - live) : 0u;
+        const unsigned v = per_head * hkv;
+        const int nl = min(64, batch - c0);
+        unsigned pre = 0, tot = 0;
+        for (int i = 0; i < nl; ++i) {
+          const unsigned x = (unsigned)__builtin_amdgcn_readlane((int)v, i);
+          pre += (i < lane) ? x : 0u;
+          tot += x;
+        }
+        const bool mine = lin >= base + pre && lin < base + pre + v;
+        const unsigned long long hit = __ballot(mine);
+        if (hit != 0ull) {
+          const int l = __ffsll((long long)hit) - 1;
+          return item_at(c0 + l, lin - base - (unsigned)__builtin_amdgcn_readlane((int)pre, l),
+                         (unsigned)__builtin_amdgcn_readlane((int)per_head, l),
+                         (unsigned)__builtin_amdgcn_readlane(live, l), pass, hkv,
+                         __builtin_amdgcn_readlane(cb, l), __builtin_amdgcn_readlane(sb, l));
+        }
+        base += tot;
+      }
+    }
+  }
+  WorkItem none = {0, 0, 0, 0, split_tokens};   // not reached: the items cover the grid
+  return none;
 }
 
 // ---- Wave-level reductions on the VALU's lane-crossing paths, no LDS round
@@ -119,6 +236,23 @@ __device__ __forceinline__ float wave_sum(float x) {
   return sum_x32(sum_x16(x));
 }
 
+// Max that keeps a NaN (fmaxf drops it): a NaN log-sum-exp marks a partial
+// that must not be merged away.
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return (a != a) ? a : ((b != b) ? b : fmaxf(a, b));
+}
+__device__ __forceinline__ float wave_max_nan(float x) {
+  x = max_nan(x, dpp_mov<dpp::kXor1>(x));
+  x = max_nan(x, dpp_mov<dpp::kXor2>(x));
+  x = max_nan(x, dpp_mov<dpp::kHalfMirror>(x));
+  x = max_nan(x, dpp_mov<dpp::kMirror>(x));
+  float a, b;
+  swap16(x, a, b);
+  x = max_nan(a, b);
+  swap32(x, a, b);
+  return max_nan(a, b);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -137,6 +271,8 @@ struct DecodeArgs {
   int32_t token_begin;       // first token of the window (multiple of split_tokens)
   int32_t token_count;       // window length (multiple of split_tokens)
   int32_t split_tokens;      // tokens per work-group (multiple of 64)
+  const int32_t* row_split;  // [batch] tokens per work-group of each request, or null
+                             // (split_tokens for all); with it every split is a tile
   float scale_log2;          // softmax scale * log2(e): scores are kept in base 2
   float* out_o;              // [batch][num_q_heads][out_slots][256]
   float* out_lse;            // [batch][num_q_heads][out_slots]

@@ -46,10 +46,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     o[u] = (u < n0) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
   const float lv = (lane < cnt) ? lse_in[lane] : -INFINITY;
 
-  // M = max_t lse_t over the group.
+  // M = max_t lse_t over the group (NaN if any slot's is: the row's result
+  // then comes out NaN instead of dropping that slot).
   float m = lv;
-  for (int t = lane + kMergeThreads; t < cnt; t += kMergeThreads) m = fmaxf(m, lse_in[t]);
-  m = wave_max(m);
+  for (int t = lane + kMergeThreads; t < cnt; t += kMergeThreads) m = max_nan(m, lse_in[t]);
+  m = wave_max_nan(m);
 
   const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
   float2* o_out = reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part) + lane;

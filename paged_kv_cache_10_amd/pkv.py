@@ -31,7 +31,7 @@ EXPORTS = [
     "pkv_admit_create", "pkv_admit_add", "pkv_admit_set_target", "pkv_admit_remove",
     "pkv_admit_step", "pkv_admit_get_counts", "pkv_admit_events", "pkv_admit_destroy",
     "pkv_compact_page_bytes", "pkv_compact_pool_create", "pkv_pool_format",
-    "pkv_compact_convert", "pkv_compact_crc",
+    "pkv_compact_convert", "pkv_compact_crc", "pkv_plan_tiles", "pkv_decode_attention_rows",
 ]
 
 
@@ -112,6 +112,10 @@ def lib():
                                            ctypes.c_float, P, P, I32, P, U64,
                                            ctypes.POINTER(DecodeOpts), P]
         L.pkv_merge_partials.argtypes = [P, P, I32, I32, I32, P, P, P]
+        L.pkv_plan_tiles.argtypes = [I32P, I32, I32, I32, I32, I32P, I32P]
+        L.pkv_decode_attention_rows.argtypes = [P, I32, P, P, I32, P, I32, I32, P, I32, I32,
+                                                ctypes.c_float, P, P, I32,
+                                                ctypes.POINTER(DecodeOpts), P]
         L.pkv_append_kv.argtypes = [P, I32, P, I32, P, I32, P, P, P]
         L.pkv_stager_create.argtypes = [P, P, U64, I32, I32, I32, I32, P, P, P, P,
                                         ctypes.POINTER(P)]
@@ -284,6 +288,45 @@ def decode_attention(pool, layer, q, dev_table, dev_ctx_lens, token_begin, token
         int(token_begin), int(token_count), int(tile_tokens), float(scale),
         _ptr(part_out, torch.float32, "part_out"), _ptr(part_lse, torch.float32, "part_lse"),
         num_slots, ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def plan_tiles(ctx_lens, num_kv_heads, work_groups=256, max_tile_tokens=16384):
+    """Per-request tile lengths for a batch (host): (int32 [B] tile tokens,
+    max tiles per request)."""
+    import numpy as np
+    c = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    tiles = np.zeros(c.size, dtype=np.int32)
+    mx = ctypes.c_int32(0)
+    _check(lib().pkv_plan_tiles(c.ctypes.data_as(I32P), int(c.size), int(num_kv_heads),
+                                int(work_groups), int(max_tile_tokens),
+                                tiles.ctypes.data_as(I32P), ctypes.byref(mx)))
+    return tiles, mx.value
+
+
+def decode_attention_rows(pool, layer, q, dev_table, dev_ctx_lens, dev_row_tiles, max_row_tile,
+                          max_tiles, scale, part_out, part_lse, kernel=0, stream=None,
+                          slot_offset=0):
+    """Partials of tiles of each request's own length (dev_row_tiles: int32
+    [B] on the device, from plan_tiles); slots slot_offset .. +max_tiles-1."""
+    import torch
+    B, Hq, D = q.shape
+    if part_out.dim() != 4 or part_out.shape[:2] != (B, Hq) or part_out.shape[3] != D:
+        raise ValueError("part_out must be [B, Hq, num_slots, D]")
+    num_slots = part_out.shape[2]
+    if tuple(part_lse.shape) != (B, Hq, num_slots):
+        raise ValueError("part_lse must be [B, Hq, num_slots]")
+    if dev_table.dim() != 2 or dev_table.shape[0] != B or dev_table.stride(1) != 1:
+        raise ValueError("dev_table must be [B, pt_stride] with contiguous rows")
+    if tuple(dev_row_tiles.shape) != (B,):
+        raise ValueError("dev_row_tiles must be [B]")
+    o = _opts(kernel, 0, slot_offset)
+    _check(lib().pkv_decode_attention_rows(
+        pool.handle, int(layer), _ptr(q, torch.bfloat16, "q"),
+        dev_table.data_ptr(), int(dev_table.stride(0)),
+        _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"), B, Hq,
+        _ptr(dev_row_tiles, torch.int32, "dev_row_tiles"), int(max_row_tile), int(max_tiles),
+        float(scale), _ptr(part_out, torch.float32, "part_out"),
+        _ptr(part_lse, torch.float32, "part_lse"), num_slots, ctypes.byref(o), _stream(stream)))
 
 
 def merge_partials(part_out, part_lse, out, lse, stream=None):

@@ -101,6 +101,40 @@ class Case:
         torch.cuda.synchronize()
         return po, pl, o, l
 
+    def decode_rows(self, layer, row_tiles, max_tiles, max_row_tile=None):
+        """Per-request tiles (row_tiles [B] on the host, copied to the
+        device), then the merge.  Returns torch (part_o, part_lse, out, lse)."""
+        w = self.w
+        B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+        row_tiles = np.asarray(row_tiles, np.int32)
+        mrt = int(row_tiles.max()) if max_row_tile is None else int(max_row_tile)
+        po = torch.full((B, Hq, max_tiles, D), float("nan"), device=DEV)
+        pl = torch.full((B, Hq, max_tiles), float("nan"), device=DEV)
+        o = torch.empty((B, Hq, D), device=DEV)
+        l = torch.empty((B, Hq), device=DEV)
+        dev_rt = torch.from_numpy(row_tiles).to(DEV)
+        pkv.decode_attention_rows(self.pool, layer, self.q[layer], self.dev_table, self.dev_ctx,
+                                  dev_rt, mrt, max_tiles, w.scale, po, pl)
+        pkv.merge_partials(po, pl, o, l)
+        torch.cuda.synchronize()
+        return po, pl, o, l
+
+    def oracle_rows(self, layer, row_tiles, max_tiles, requests=None):
+        """float64 (tile partials, one-pass out, lse) per request, tile b of
+        row_tiles[b] tokens."""
+        w = self.w
+        qf = self.q_f64(layer)
+        res = {}
+        for b in (range(w.batch) if requests is None else requests):
+            k, v = self.logical_kv_f64(layer, b)
+            ctx = w.ctx_lens[b]
+            o_t, l_t = oracle.tile_partials(qf[b], k, v, w.scale,
+                                            oracle.tile_bounds(ctx, int(row_tiles[b]), max_tiles),
+                                            w.num_kv_heads)
+            out, lse = oracle.decode_one_pass(qf[b], k, v, ctx, w.scale, w.num_kv_heads)
+            res[b] = (o_t, l_t, out, lse)
+        return res
+
     def oracle_layer(self, layer, tile=None, requests=None):
         """float64 (tile partials, one-pass out, lse) per request."""
         w = self.w

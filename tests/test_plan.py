@@ -1,0 +1,142 @@
+"""Per-request tile plan (host only, no GPU): pkv_plan_tiles against a
+brute-force search of the same definition, its invariants on random
+batches, and the host-side refusals of pkv_decode_attention_rows."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_10_amd import inputs as I
+from paged_kv_cache_10_amd import pkv
+from test_abi import FakePool, err
+
+PT = 64
+
+
+def brute_plan(ctx, hkv, work_groups, max_tile):
+    """The definition, searched exhaustively: the smallest multiple of 64 up
+    to max_tile whose split count fits the work-groups (else max_tile), then
+    each request's tokens in equal shares rounded up to 64."""
+    def groups(tau):
+        return hkv * sum(-(-c // tau) for c in ctx)
+    tau = next((t for t in range(PT, max_tile + 1, PT) if groups(t) <= work_groups), max_tile)
+    tiles, most = [], 1
+    for c in ctx:
+        n = -(-c // tau)
+        tiles.append(-(-(-(-c // n)) // PT) * PT if n else PT)
+        most = max(most, n)
+    return tiles, most, tau
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_matches_brute_force_and_invariants(seed):
+    r = np.random.default_rng(seed)
+    B = int(r.integers(1, 24))
+    ctx = [int(x) for x in r.choice([0, 1, 63, 64, 65, 4097, int(r.integers(1, 200000))], B)]
+    hkv = int(r.choice([1, 2, 4, 8]))
+    W = int(r.choice([1, 8, 64, 256, 512, 1024]))
+    max_tile = int(r.choice([64, 1024, 4096, 16384]))
+    tiles, most = pkv.plan_tiles(ctx, hkv, W, max_tile)
+    bt, bm, tau = brute_plan(ctx, hkv, W, max_tile)
+    assert tiles.tolist() == bt and most == bm
+    n = [-(-c // t) for c, t in zip(ctx, tiles.tolist())]
+    for c, t, k in zip(ctx, tiles.tolist(), n):
+        assert t % PT == 0 and PT <= t <= tau <= max_tile
+        assert k * t >= c and (k == 0 or (k - 1) * t < c)     # k tiles cover c, none idle
+        assert k == -(-c // tau)                              # as many tiles as at tau
+    assert most == max([1] + n)
+    if hkv * sum(-(-c // max_tile) for c in ctx) <= W:
+        assert hkv * sum(n) <= W
+
+
+def test_plan_of_the_mixed_batch():
+    """The 16-request mixed batch at one work-group per CU: 252 work-groups,
+    every tile within 7,552 tokens (the mean is 6,661)."""
+    w = I.workload("mixed")
+    tiles, most = pkv.plan_tiles(w.ctx_lens, w.num_kv_heads, 256)
+    n = [-(-c // t) for c, t in zip(w.ctx_lens, tiles.tolist())]
+    assert w.num_kv_heads * sum(n) == 252 and most == max(n) == 15
+    assert int(tiles.max()) == 7552
+    assert sum(w.ctx_lens) * w.num_kv_heads / 256 == pytest.approx(6661.5, abs=0.1)
+
+
+def test_plan_edge_cases():
+    t, m = pkv.plan_tiles([], 4, 256)
+    assert t.size == 0 and m == 1
+    t, m = pkv.plan_tiles([0, 0], 4, 256)
+    assert t.tolist() == [64, 64] and m == 1
+    t, m = pkv.plan_tiles([262144], 4, 256)                 # one request: 64 splits of 4,096
+    assert t.tolist() == [4096] and m == 64
+    t, m = pkv.plan_tiles([262144], 4, 1)                   # cannot fit: the largest tile
+    assert t.tolist() == [16384] and m == 16
+    t, m = pkv.plan_tiles([1], 1, 1, 64)
+    assert t.tolist() == [64] and m == 1
+
+
+def plan_raw(ctx, batch, hkv=4, W=256, max_tile=16384, tiles=True, mx=True):
+    c = (ctypes.c_int32 * max(1, len(ctx)))(*ctx)
+    out = (ctypes.c_int32 * max(1, len(ctx)))()
+    m = ctypes.c_int32(0)
+    rc = pkv.lib().pkv_plan_tiles(c, batch, hkv, W, max_tile, out if tiles else None,
+                                  ctypes.byref(m) if mx else None)
+    return rc, err()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(batch=-1), "batch"),
+    (dict(hkv=0), "num_kv_heads"),
+    (dict(W=0), "work_groups"),
+    (dict(max_tile=100), "max_tile_tokens"),
+    (dict(max_tile=32768), "max_tile_tokens"),
+    (dict(tiles=False), "NULL"),
+    (dict(mx=False), "NULL"),
+])
+def test_plan_arguments_are_refused(kw, needle):
+    a = dict(batch=2)
+    a.update(kw)
+    rc, msg = plan_raw([5, 7], **a)
+    assert rc == -1 and needle in msg, msg
+
+
+def test_plan_refuses_negative_lengths():
+    rc, msg = plan_raw([5, -7], 2)
+    assert rc == -1 and "ctx_lens[1]" in msg
+
+
+def rows_raw(pool, **kw):
+    a = dict(layer=0, q=1 << 20, table=1 << 21, pt_stride=64, ctx=1 << 22, batch=1, hq=24,
+             rows=1 << 26, max_row=1024, max_tiles=4, scale=0.0625, po=1 << 23, pl=1 << 24,
+             slots=4, kernel=0, split=0, slot_offset=0)
+    a.update(kw)
+    o = pkv.DecodeOpts(a["kernel"], a["split"], a["slot_offset"])
+    rc = pkv.lib().pkv_decode_attention_rows(
+        pool.handle, a["layer"], a["q"], a["table"], a["pt_stride"], a["ctx"], a["batch"], a["hq"],
+        a["rows"], a["max_row"], a["max_tiles"], a["scale"], a["po"], a["pl"], a["slots"],
+        ctypes.byref(o), None)
+    return rc, err()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(layer=16), -1, "layer"),
+    (dict(hq=25), -3, "num_q_heads"),
+    (dict(kernel=1), -1, "MFMA"),
+    (dict(split=1024), -1, "split_tokens"),
+    (dict(max_row=100), -1, "max_row_tile_tokens"),
+    (dict(max_row=32768), -1, "max_row_tile_tokens"),
+    (dict(max_tiles=0), -1, "max_tiles"),
+    (dict(pt_stride=63), -1, "pt_stride"),
+    (dict(slots=3), -1, "num_slots"),
+    (dict(slot_offset=1), -1, "num_slots"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(rows=0), -1, "NULL"),
+    (dict(q=(1 << 20) + 2), -1, "aligned"),
+    (dict(batch=-1), -1, "batch"),
+])
+def test_rows_arguments_are_refused_on_the_host(kw, code, needle):
+    rc, msg = rows_raw(FakePool(64), **kw)
+    assert rc == code and needle in msg, msg
+
+
+def test_rows_with_no_requests_do_nothing():
+    assert rows_raw(FakePool(64), batch=0)[0] == 0
