@@ -2,13 +2,16 @@
 // compact page (the representation and layouts are described in compact.h).
 //
 // convert_kernel: one 256-thread work-group per (K|V x kv head, layer, page
-// pair).  Pass 1 reads the exact block (32 KiB) and reduces its largest
-// magnitude; pass 2 re-reads it (from L2) and writes the 1,024 compact
-// pieces, each thread building whole 16-byte pieces from two exact pieces.
+// pair).  The exact block (32 KiB) is read once, in 1 KiB loads, into LDS
+// while its largest magnitude is reduced; the 1,024 compact pieces are then
+// built from LDS, each thread building whole 16-byte pieces from two exact
+// pieces.
 //
 // crc_kernel: one 256-thread work-group per page.  In every layer thread t
 // takes the t-th of 256 equal segments of the code region and computes its
-// CRC from a zero register (table-driven, four bytes per step); the 256
+// CRC from a zero register (table-driven, four bytes per step), reading its
+// segment a 128-byte line at a time (the line's eight loads in flight
+// together, so every line is fetched once); the 256
 // segment CRCs are combined pairwise in a tree, using
 //   crc(A || B) = crc(A) * x^(8|B|) + crc(B)   (mod the CRC polynomial),
 // then the layer's scales are appended and the layers folded in order; the
@@ -72,10 +75,13 @@ __global__ __launch_bounds__(256) void convert_kernel(ConvertArgs a) {
   uint8_t* out = a.codes + ((int64_t)layer * a.dst_num_pages + dp) * a.dst_page_bytes +
                  (int64_t)kvh * kCompactBlockBytes;
 
-  // pass 1: the block's largest magnitude
+  // the block into LDS (piece p at p), reducing its largest magnitude
+  __shared__ uint4 blk_lds[kPageTokens * kHeadDim / 8];
   float amax = 0.f;
-  for (int p = tid; p < kPageTokens * kHeadDim / 8; p += 256) {
-    const uint4 u = blk[p];
+#pragma unroll
+  for (int m = 0; m < kPageTokens * kHeadDim / 8 / 256; ++m) {
+    const uint4 u = blk[tid + 256 * m];
+    blk_lds[tid + 256 * m] = u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_elem(u, e)));
   }
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(256) void convert_kernel(ConvertArgs a) {
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float s = (amax == 0.f) ? 1.f : amax / kE4M3Max;
 
-  // pass 2: 1,024 pieces of 16 codes
+  // 1,024 pieces of 16 codes
   const bool is_k = kvh < a.num_kv_heads;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -103,8 +109,8 @@ __global__ __launch_bounds__(256) void convert_kernel(ConvertArgs a) {
       p0 = v_piece(d, q);
       p1 = v_piece(d, 4 + q);
     }
-    const uint2 lo = encode8(blk[p0], s);
-    const uint2 hi = encode8(blk[p1], s);
+    const uint2 lo = encode8(blk_lds[p0], s);
+    const uint2 hi = encode8(blk_lds[p1], s);
     reinterpret_cast<uint4*>(out)[cp] = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
   if (tid == 0)
@@ -149,14 +155,19 @@ __global__ __launch_bounds__(256) void crc_kernel(CrcArgs a) {
     const uint4* p = reinterpret_cast<const uint4*>(
         a.codes + ((int64_t)l * a.num_pages + pg) * a.page_bytes + (int64_t)tid * seg);
     uint32_t c = 0u;
-    for (int64_t v = 0; v < seg / 16; ++v) {
-      const uint4 u = p[v];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int64_t v0 = 0; v0 < seg / 16; v0 += 8) {     // one 128-byte line at a time
+      uint4 line[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t x = c ^ w[k];
-        c = tab[3][x & 0xFFu] ^ tab[2][(x >> 8) & 0xFFu] ^ tab[1][(x >> 16) & 0xFFu] ^
-            tab[0][x >> 24];
+      for (int v = 0; v < 8; ++v) line[v] = p[v0 + v];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const uint32_t w[4] = {line[v].x, line[v].y, line[v].z, line[v].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t x = c ^ w[k];
+          c = tab[3][x & 0xFFu] ^ tab[2][(x >> 8) & 0xFFu] ^ tab[1][(x >> 16) & 0xFFu] ^
+              tab[0][x >> 24];
+        }
       }
     }
     part[tid] = c;
