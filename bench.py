@@ -117,6 +117,9 @@ def parse():
     ap.add_argument("--tile", type=int, default=0, help="tile tokens (default: LAUNCH)")
     ap.add_argument("--split", type=int, default=0, help="tokens per work-group (default: LAUNCH)")
     ap.add_argument("--kernel", default="mfma", choices=["mfma", "valu"])
+    ap.add_argument("--separate", action="store_true",
+                    help="decode and merge as separate calls (default: one merged call per "
+                         "layer where the tiling allows)")
     ap.add_argument("--plan", type=int, default=None,
                     help="per-request tiles planned for this many work-groups (0: the fixed "
                          "tiling; default: LAUNCH)")
@@ -232,8 +235,19 @@ def main():
                                  pl[layer], workspace=ws, kernel=args.kernel,
                                  split_tokens=args.split, stream=stream)
 
+    # a whole-history fixed tiling decodes and merges each layer in one call
+    # (one kernel boundary fewer where tiles hold several splits); the
+    # per-call roofline events and the overlapped schedule use separate calls
+    use_merged = not plan and not args.staged and not args.separate
+
     def step(evs=None, overlap=overlap):
         for layer in range(L):
+            if use_merged and evs is None and not overlap:
+                pkv.decode_attention_merged(pool, layer, qs[layer], dt, dc, span, T, w.scale,
+                                            po[layer], pl[layer], outs[layer], lses[layer],
+                                            workspace=ws, kernel=args.kernel,
+                                            split_tokens=args.split, stream=stream)
+                continue
             if evs is not None:
                 evs[layer][0].record(stream)
             decode_layer(layer)
@@ -289,7 +303,13 @@ def main():
     dec_ms = [a.elapsed_time(b) for evk in ev_dec for (a, b) in evk]
     dec_avg_ms = float(np.mean(dec_ms))
 
-    # the overlapped schedule against a serialized recompute on one stream
+    # the timed schedule and the overlapped one against a serialized
+    # recompute (separate decode and merge calls on one stream)
+    def same(a, b):
+        return bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+    step()
+    torch.cuda.synchronize()
+    timed_o, timed_l = outs.clone(), lses.clone()
     step(overlap=True)
     torch.cuda.synchronize()
     ref_o, ref_l = outs.clone(), lses.clone()
@@ -298,8 +318,8 @@ def main():
         decode_layer(layer)
         pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=stream)
     torch.cuda.synchronize()
-    self_check = bool(torch.equal(ref_o.view(torch.int32), outs.view(torch.int32))
-                      and torch.equal(ref_l.view(torch.int32), lses.view(torch.int32)))
+    self_check = same(ref_o, outs) and same(ref_l, lses)
+    timed_check = same(timed_o, outs) and same(timed_l, lses)
 
     if args.host_staged and args.compact_older:
         res = host_staged_hybrid(args, w, pool, arena, table, ctx, qs, outs, lses, T, span)
@@ -349,6 +369,8 @@ def main():
             "tile_tokens": row_tiles.tolist() if plan else T,
             "kernel": args.kernel, "split_tokens": args.split or "default",
             "merge_overlapped": overlap,
+            "decode_and_merge": ("pkv_decode_attention_merged, one call per layer"
+                                 if use_merged and not overlap else "separate calls"),
             "parallelism": "none (1 GPU)",
         },
         "tokens_per_s": round(tok_s, 2),
@@ -375,6 +397,7 @@ def main():
         },
         "setup_s": round(t_gen, 1),
         "overlapped_equals_serial_bitwise": self_check,
+        "timed_equals_serial_bitwise": timed_check,
         ("serial_merges" if overlap else "overlapped_merges"): {
             "ms_per_step": round(ms_other, 4),
             "value": round(kv_bytes_step / (ms_other * 1e-3) / 1e9, 1),

@@ -244,6 +244,24 @@ int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
                          void* workspace, uint64_t workspace_bytes,
                          const pkv_decode_opts* opts, void* stream);
 
+/* Decode and merge of a whole history in one call: the tile partials exactly
+ * as pkv_decode_attention with token_begin = 0, then out [batch][num_q_heads]
+ * [head_dim] and lse [batch][num_q_heads] exactly as pkv_merge_partials over
+ * all num_slots slots, bit for bit (the same FP32 merge runs in both).  The
+ * call must write every slot: token_count / tile_tokens == num_slots and
+ * opts.slot_offset == 0.  Where a tile holds several splits and a row has at
+ * most 64 splits, the tile finalize and the final merge are one launch (one
+ * kernel boundary fewer per layer than decode + merge).  out: FP32 device,
+ * 16-byte aligned; lse: FP32 device.  Other arguments and errors as
+ * pkv_decode_attention. */
+int pkv_decode_attention_merged(const pkv_pool* pool, int32_t layer, const void* q,
+                                const int32_t* dev_table, int32_t pt_stride,
+                                const int32_t* dev_ctx_lens, int32_t batch, int32_t num_q_heads,
+                                int32_t token_count, int32_t tile_tokens, float scale,
+                                float* part_out, float* part_lse, int32_t num_slots, float* out,
+                                float* lse, void* workspace, uint64_t workspace_bytes,
+                                const pkv_decode_opts* opts, void* stream);
+
 /* ------------------------------------------------ per-request tiles --
  * Tiles of their own length for each request of a batch (the same per-tile
  * partials and merge as above; the KV-cache engineering page, section

@@ -49,6 +49,7 @@ int ok() {
 
 constexpr int kDefaultSplit = 2048;  // tokens per work-group unless the caller says otherwise
 constexpr int kMaxMfmaSplit = 64 * 4 * 64;   // 64 pages per wave x 4 waves x 64 tokens
+constexpr int kMaxMerge2Splits = 64;          // split partials per row one merge2 launch holds
 
 int check_geom(const pkv_geom* g) {
   if (!g) return fail(PKV_ERR_INVALID_ARG, "geom is NULL");
@@ -316,13 +317,16 @@ PKV_API int pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
   return ok();
 }
 
-PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
-                                 const int32_t* dev_table, int32_t pt_stride,
-                                 const int32_t* dev_ctx_lens, int32_t batch, int32_t num_q_heads,
-                                 int32_t token_begin, int32_t token_count, int32_t tile_tokens,
-                                 float scale, float* part_out, float* part_lse, int32_t num_slots,
-                                 void* workspace, uint64_t workspace_bytes,
-                                 const pkv_decode_opts* opts, void* stream) {
+namespace {
+
+// pkv_decode_attention, and with fin_out / fin_lse also the final merge of
+// every slot of each row (pkv_decode_attention_merged).
+int decode_impl(const pkv_pool* pool, int32_t layer, const void* q, const int32_t* dev_table,
+                int32_t pt_stride, const int32_t* dev_ctx_lens, int32_t batch,
+                int32_t num_q_heads, int32_t token_begin, int32_t token_count,
+                int32_t tile_tokens, float scale, float* part_out, float* part_lse,
+                int32_t num_slots, void* workspace, uint64_t workspace_bytes,
+                const pkv_decode_opts* opts, void* stream, float* fin_out, float* fin_lse) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   const pkv_geom& G = pool->geom;
   if (layer < 0 || layer >= G.num_layers)
@@ -363,9 +367,18 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
                 first_slot, first_slot + n_tiles - 1, num_slots);
   if (num_slots > 65535) return fail(PKV_ERR_INVALID_ARG, "num_slots = %d exceeds 65535", num_slots);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  const bool merged = fin_out != nullptr || fin_lse != nullptr;
+  if (merged && (slot_offset != 0 || n_tiles != num_slots))
+    return fail(PKV_ERR_INVALID_ARG,
+                "merged decode writes every slot of its rows: token_count / tile_tokens = %d must "
+                "equal num_slots = %d and opts.slot_offset (%d) must be 0", n_tiles, num_slots,
+                slot_offset);
   if (batch == 0 || token_count == 0) return ok();
   if (!q || !dev_table || !dev_ctx_lens || !part_out || !part_lse)
     return fail(PKV_ERR_INVALID_ARG, "q, dev_table, dev_ctx_lens, part_out or part_lse is NULL");
+  if (merged && (!fin_out || !fin_lse)) return fail(PKV_ERR_INVALID_ARG, "out or lse is NULL");
+  if (merged && reinterpret_cast<uintptr_t>(fin_out) % 16)
+    return fail(PKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(part_out) % 16)
     return fail(PKV_ERR_INVALID_ARG, "q and part_out must be 16-byte aligned");
 
@@ -450,6 +463,8 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
                       : pkv::launch_decode_mfma(a, batch, group, s);
   }
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+  const int rows = batch * num_q_heads;
+  bool final_done = false;
   if (split != tile_tokens) {
     pkv::MergeArgs m;
     m.in_o = ws_o;
@@ -461,11 +476,58 @@ PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void
     m.out_slots = num_slots;
     m.out_slot0 = first_slot;
     m.n_out = n_tiles;
-    e = pkv::launch_merge(m, batch * num_q_heads, s);
+    if (merged && n_split <= kMaxMerge2Splits) {   // finalize and final merge in one launch
+      e = pkv::launch_merge2(m, rows, fin_out, fin_lse, s);
+      final_done = true;
+    } else {
+      e = pkv::launch_merge(m, rows, s);
+    }
     if (e != hipSuccess)
       return fail(PKV_ERR_LAUNCH, "tile finalize launch failed: %s", hipGetErrorString(e));
   }
+  if (merged && !final_done) {
+    pkv::MergeArgs m;
+    m.in_o = part_out;
+    m.in_lse = part_lse;
+    m.in_slots = num_slots;
+    m.group = num_slots;
+    m.out_o = fin_out;
+    m.out_lse = fin_lse;
+    m.out_slots = 1;
+    m.out_slot0 = 0;
+    m.n_out = 1;
+    e = pkv::launch_merge(m, rows, s);
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
+}
+
+}  // namespace
+
+PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
+                                 const int32_t* dev_table, int32_t pt_stride,
+                                 const int32_t* dev_ctx_lens, int32_t batch, int32_t num_q_heads,
+                                 int32_t token_begin, int32_t token_count, int32_t tile_tokens,
+                                 float scale, float* part_out, float* part_lse, int32_t num_slots,
+                                 void* workspace, uint64_t workspace_bytes,
+                                 const pkv_decode_opts* opts, void* stream) {
+  return decode_impl(pool, layer, q, dev_table, pt_stride, dev_ctx_lens, batch, num_q_heads,
+                     token_begin, token_count, tile_tokens, scale, part_out, part_lse, num_slots,
+                     workspace, workspace_bytes, opts, stream, nullptr, nullptr);
+}
+
+PKV_API int pkv_decode_attention_merged(const pkv_pool* pool, int32_t layer, const void* q,
+                                        const int32_t* dev_table, int32_t pt_stride,
+                                        const int32_t* dev_ctx_lens, int32_t batch,
+                                        int32_t num_q_heads, int32_t token_count,
+                                        int32_t tile_tokens, float scale, float* part_out,
+                                        float* part_lse, int32_t num_slots, float* out, float* lse,
+                                        void* workspace, uint64_t workspace_bytes,
+                                        const pkv_decode_opts* opts, void* stream) {
+  if (!out || !lse) return fail(PKV_ERR_INVALID_ARG, "out or lse is NULL");
+  return decode_impl(pool, layer, q, dev_table, pt_stride, dev_ctx_lens, batch, num_q_heads, 0,
+                     token_count, tile_tokens, scale, part_out, part_lse, num_slots, workspace,
+                     workspace_bytes, opts, stream, out, lse);
 }
 
 PKV_API int pkv_plan_tiles(const int32_t* host_ctx_lens, int32_t batch, int32_t num_kv_heads,

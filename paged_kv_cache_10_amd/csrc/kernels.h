@@ -23,6 +23,10 @@ struct MergeArgs {
 };
 
 hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t stream);
+// The same groups of rows of at most 64 input slots, then their n_out
+// results merged into fin_o [rows][256] and fin_lse [rows], in one launch.
+hipError_t launch_merge2(const MergeArgs& a, int rows, float* fin_o, float* fin_lse,
+                         hipStream_t stream);
 
 // Split-KV decode: one work-group per (split, kv head, request) writes the
 // normalised output and log-sum-exp of its split for the kv head's query

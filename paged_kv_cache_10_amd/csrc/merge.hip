@@ -3,16 +3,18 @@
 // by exp(lse_t - max lse), the weighted outputs are summed and divided by the
 // summed weights, and the merged log-sum-exp is max + log(sum).
 //
-// One kernel serves two places on the path:
-//   * the final merge of every slot of a row into one output (pkv_merge_partials);
+// The merge arithmetic (merge_slots) serves three places:
+//   * the final merge of every slot of a row into one output
+//     (pkv_merge_partials, merge_kernel);
 //   * the tile finalize inside pkv_decode_attention, which merges the fixed
-//     groups of split partials that make up one tile.
+//     groups of split partials that make up one tile (merge_kernel);
+//   * both at once for pkv_decode_attention_merged (merge2_kernel).
 // Two waves own one (row, output slot), 128 channels each (two per lane, so
 // more of the GPU's load queues work on a row and every load is 512
-// contiguous bytes), and each walks its input
-// slots in increasing order with one accumulator per channel, so the result
-// is independent of scheduling, an empty slot (lse = -inf) contributes
-// exactly nothing and a lone slot merges to itself bit for bit.
+// contiguous bytes), and each walks its input slots in increasing order with
+// one accumulator per channel, so the result is independent of scheduling,
+// an empty slot (lse = -inf) contributes exactly nothing and a lone slot
+// merges to itself bit for bit.
 #include "device.h"
 #include "kernels.h"
 
@@ -24,54 +26,38 @@ constexpr int kMergeThreads = 64;     // one wave; lane i owns channels 128 * ha
 constexpr int kMergeParts = kHeadDim / 128;   // waves per (row, output slot)
 constexpr int kMergeChunk = 64;       // input slots whose loads are in flight together
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
-  const int row = blockIdx.x;
-  const int j = blockIdx.y;
-  const int part = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int t0 = j * a.group;
-  const int cnt = min(a.group, a.in_slots - t0);
+struct Merged {
+  float2 o;    // this lane's two channels
+  float lse;
+};
 
-  const float* lse_in = a.in_lse + (int64_t)row * a.in_slots + t0;
-  const float2* o_in = reinterpret_cast<const float2*>(
-      a.in_o + ((int64_t)row * a.in_slots + t0) * kHeadDim + 128 * part) + lane;
-
-  // The output loads of the first 64 slots do not depend on the max: they go
-  // out first, beside this lane's log-sum-exp, so the max and the loads
-  // overlap instead of taking two round trips to memory.
-  float2 o[kMergeChunk];
-  const int n0 = min(kMergeChunk, cnt);
+// The first min(64, cnt) slots' outputs (o_in[t * 128], two channels per
+// lane) into o; they do not depend on the max, so they go out first.
+__device__ __forceinline__ void load_chunk(float2 (&o)[kMergeChunk], const float2* o_in, int n) {
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u)
-    o[u] = (u < n0) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
-  const float lv = (lane < cnt) ? lse_in[lane] : -INFINITY;
+    o[u] = (u < n) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
+}
 
-  // M = max_t lse_t over the group (NaN if any slot's is: the row's result
-  // then comes out NaN instead of dropping that slot).
+// The merge of cnt slots: lv = this lane's slot's log-sum-exp (lane < cnt,
+// else -inf), further log-sum-exps in lse_in[64 ..), outputs at o_in with
+// the first 64 already in o.  M = max_t lse_t (NaN if any slot's is: the
+// row's result then comes out NaN instead of dropping that slot); chunks of
+// 64 slots: lane u computes the weight of the chunk's slot u (one exp per
+// lane, all in parallel), then the slots are summed in increasing order with
+// each weight read from its lane.  Every merge in this file goes through
+// here, so a merge gives the same bits wherever it runs.
+__device__ __forceinline__ Merged merge_slots(float lv, const float* lse_in, const float2* o_in,
+                                              int cnt, int lane, float2 (&o)[kMergeChunk]) {
   float m = lv;
   for (int t = lane + kMergeThreads; t < cnt; t += kMergeThreads) m = max_nan(m, lse_in[t]);
   m = wave_max_nan(m);
-
-  const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
-  float2* o_out = reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part) + lane;
-  if (m == -INFINITY) {                       // every slot empty
-    *o_out = make_float2(0.f, 0.f);
-    if (part == 0 && lane == 0) a.out_lse[orow] = -INFINITY;
-    return;
-  }
-
-  // Chunks of 64 slots: lane u computes the weight of the chunk's slot u
-  // (one exp per lane, all in parallel), then the slots are summed in
-  // increasing order with each weight read from its lane.
+  if (m == -INFINITY) return Merged{make_float2(0.f, 0.f), -INFINITY};   // every slot empty
   float2 acc = make_float2(0.f, 0.f);
   float wsum = 0.f;
   for (int c0 = 0; c0 < cnt; c0 += kMergeChunk) {
     const int nc = min(kMergeChunk, cnt - c0);
-    if (c0 > 0) {
-#pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u)
-        o[u] = (u < nc) ? o_in[(int64_t)(c0 + u) * (kHeadDim / 2)] : make_float2(0.f, 0.f);
-    }
+    if (c0 > 0) load_chunk(o, o_in + (int64_t)c0 * (kHeadDim / 2), nc);
     const float lt = (c0 == 0) ? lv : ((lane < nc) ? lse_in[c0 + lane] : -INFINITY);
     const float wl = (lane < nc) ? expf(lt - m) : 0.f;     // 0 for an empty slot
 #pragma unroll
@@ -84,8 +70,91 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       }
     }
   }
-  *o_out = make_float2(acc.x / wsum, acc.y / wsum);
-  if (part == 0 && lane == 0) a.out_lse[orow] = m + logf(wsum);
+  return Merged{make_float2(acc.x / wsum, acc.y / wsum), m + logf(wsum)};
+}
+
+// Group j of row `row`: slots j*group .. of the input, into output slot j.
+__device__ __forceinline__ Merged merge_group(const MergeArgs& a, int row, int j, int part,
+                                              int lane) {
+  const int t0 = j * a.group;
+  const int cnt = min(a.group, a.in_slots - t0);
+  const float* lse_in = a.in_lse + (int64_t)row * a.in_slots + t0;
+  const float2* o_in = reinterpret_cast<const float2*>(
+      a.in_o + ((int64_t)row * a.in_slots + t0) * kHeadDim + 128 * part) + lane;
+  float2 o[kMergeChunk];
+  load_chunk(o, o_in, min(kMergeChunk, cnt));
+  const float lv = (lane < cnt) ? lse_in[lane] : -INFINITY;
+  return merge_slots(lv, lse_in, o_in, cnt, lane, o);
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  const int row = blockIdx.x, j = blockIdx.y, part = blockIdx.z, lane = threadIdx.x;
+  const Merged r = merge_group(a, row, j, part, lane);
+  const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
+  reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part)[lane] = r.o;
+  if (part == 0 && lane == 0) a.out_lse[orow] = r.lse;
+}
+
+// The merge of the cnt slots lo .. lo+cnt-1 of a window of at most 64 slots
+// whose log-sum-exps sit in the lanes (lv at lane u = slot u) and whose
+// outputs are in LDS (win[u][lane]): merge_slots' arithmetic (the same max,
+// the same exp per slot, the slots summed in increasing order), so a group
+// merged here has the bits merge_slots gives it.
+__device__ __forceinline__ Merged merge_window(float lv, int lo, int cnt, int lane,
+                                               const float2 (*win)[kMergeThreads]) {
+  const bool mine = lane >= lo && lane < lo + cnt;
+  const float m = wave_max_nan(mine ? lv : -INFINITY);
+  if (m == -INFINITY) return Merged{make_float2(0.f, 0.f), -INFINITY};   // every slot empty
+  const float wl = mine ? expf(lv - m) : 0.f;
+  float2 acc = make_float2(0.f, 0.f);
+  float wsum = 0.f;
+  for (int u = lo; u < lo + cnt; ++u) {
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+    if (w != 0.f) {                            // uniform: 0 for an empty slot
+      const float2 ou = win[u][lane];
+      acc.x = fmaf(w, ou.x, acc.x);
+      acc.y = fmaf(w, ou.y, acc.y);
+      wsum += w;
+    }
+  }
+  return Merged{make_float2(acc.x / wsum, acc.y / wsum), m + logf(wsum)};
+}
+
+// Tile finalize and final merge in one launch, for rows of at most 64 split
+// partials: all of a row's split partials are loaded at once (into LDS),
+// every group j is merged into output slot j (as merge_kernel would), and
+// the group results, kept in LDS and in lane j, are merged again into
+// fin_o / fin_lse (as merge_kernel over those slots would), so the bits
+// equal the two launches'.
+__global__ __launch_bounds__(kMergeThreads) void merge2_kernel(MergeArgs a, float* fin_o,
+                                                                float* fin_lse) {
+  const int row = blockIdx.x, part = blockIdx.z, lane = threadIdx.x;
+  __shared__ float2 split_o[kMergeChunk][kMergeThreads];
+  __shared__ float2 tile_o[kMergeChunk][kMergeThreads];
+  const float* lse_in = a.in_lse + (int64_t)row * a.in_slots;
+  const float2* o_in = reinterpret_cast<const float2*>(
+      a.in_o + (int64_t)row * a.in_slots * kHeadDim + 128 * part) + lane;
+  {
+    float2 o[kMergeChunk];
+    load_chunk(o, o_in, a.in_slots);
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u)
+      if (u < a.in_slots) split_o[u][lane] = o[u];
+  }
+  const float lv = (lane < a.in_slots) ? lse_in[lane] : -INFINITY;
+  float tl = -INFINITY;                        // lane j: the log-sum-exp of group j
+  for (int j = 0; j < a.n_out; ++j) {
+    const int lo = j * a.group;
+    const Merged r = merge_window(lv, lo, min(a.group, a.in_slots - lo), lane, split_o);
+    const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
+    reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part)[lane] = r.o;
+    if (part == 0 && lane == 0) a.out_lse[orow] = r.lse;
+    tile_o[j][lane] = r.o;
+    if (lane == j) tl = r.lse;
+  }
+  const Merged r = merge_window(tl, 0, a.n_out, lane, tile_o);
+  reinterpret_cast<float2*>(fin_o + (int64_t)row * kHeadDim + 128 * part)[lane] = r.o;
+  if (part == 0 && lane == 0) fin_lse[row] = r.lse;
 }
 
 }  // namespace
@@ -94,6 +163,15 @@ hipError_t launch_merge(const MergeArgs& a, int rows, hipStream_t stream) {
   if (rows <= 0 || a.n_out <= 0) return hipSuccess;
   dim3 grid(rows, a.n_out, kMergeParts);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge2(const MergeArgs& a, int rows, float* fin_o, float* fin_lse,
+                         hipStream_t stream) {
+  if (rows <= 0 || a.n_out <= 0) return hipSuccess;
+  if (a.in_slots > kMergeChunk) return hipErrorInvalidValue;   // one window per row
+  dim3 grid(rows, 1, kMergeParts);
+  hipLaunchKernelGGL(merge2_kernel, grid, dim3(kMergeThreads), 0, stream, a, fin_o, fin_lse);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ EXPORTS = [
     "pkv_admit_step", "pkv_admit_get_counts", "pkv_admit_events", "pkv_admit_destroy",
     "pkv_compact_page_bytes", "pkv_compact_pool_create", "pkv_pool_format",
     "pkv_compact_convert", "pkv_compact_crc", "pkv_plan_tiles", "pkv_decode_attention_rows",
+    "pkv_decode_attention_merged",
 ]
 
 
@@ -112,6 +113,9 @@ def lib():
                                            ctypes.c_float, P, P, I32, P, U64,
                                            ctypes.POINTER(DecodeOpts), P]
         L.pkv_merge_partials.argtypes = [P, P, I32, I32, I32, P, P, P]
+        L.pkv_decode_attention_merged.argtypes = [P, I32, P, P, I32, P, I32, I32, I32, I32,
+                                                  ctypes.c_float, P, P, I32, P, P, P, U64,
+                                                  ctypes.POINTER(DecodeOpts), P]
         L.pkv_plan_tiles.argtypes = [I32P, I32, I32, I32, I32, I32P, I32P]
         L.pkv_decode_attention_rows.argtypes = [P, I32, P, P, I32, P, I32, I32, P, I32, I32,
                                                 ctypes.c_float, P, P, I32,
@@ -288,6 +292,35 @@ def decode_attention(pool, layer, q, dev_table, dev_ctx_lens, token_begin, token
         int(token_begin), int(token_count), int(tile_tokens), float(scale),
         _ptr(part_out, torch.float32, "part_out"), _ptr(part_lse, torch.float32, "part_lse"),
         num_slots, ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def decode_attention_merged(pool, layer, q, dev_table, dev_ctx_lens, token_count, tile_tokens,
+                            scale, part_out, part_lse, out, lse, workspace=None, kernel=0,
+                            split_tokens=0, stream=None):
+    """Tile partials of the whole history and their merge in one call:
+    part_out / part_lse as decode_attention (token_begin 0, every slot), out
+    [B, Hq, D] and lse [B, Hq] as merge_partials over them."""
+    import torch
+    B, Hq, D = q.shape
+    if part_out.dim() != 4 or part_out.shape[:2] != (B, Hq) or part_out.shape[3] != D:
+        raise ValueError("part_out must be [B, Hq, num_slots, D]")
+    num_slots = part_out.shape[2]
+    if tuple(part_lse.shape) != (B, Hq, num_slots):
+        raise ValueError("part_lse must be [B, Hq, num_slots]")
+    if tuple(out.shape) != (B, Hq, D) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out must be [B, Hq, D] and lse [B, Hq]")
+    if dev_table.dim() != 2 or dev_table.shape[0] != B or dev_table.stride(1) != 1:
+        raise ValueError("dev_table must be [B, pt_stride] with contiguous rows")
+    o = _opts(kernel, split_tokens, 0)
+    ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pkv_decode_attention_merged(
+        pool.handle, int(layer), _ptr(q, torch.bfloat16, "q"),
+        dev_table.data_ptr(), int(dev_table.stride(0)),
+        _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"), B, Hq, int(token_count),
+        int(tile_tokens), float(scale), _ptr(part_out, torch.float32, "part_out"),
+        _ptr(part_lse, torch.float32, "part_lse"), num_slots, _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
 
 
 def plan_tiles(ctx_lens, num_kv_heads, work_groups=256, max_tile_tokens=16384):

@@ -101,6 +101,25 @@ class Case:
         torch.cuda.synchronize()
         return po, pl, o, l
 
+    def decode_merged(self, layer, tile=None, split=0):
+        """pkv_decode_attention_merged over the whole history: torch
+        (part_o, part_lse, out, lse)."""
+        w = self.w
+        tile = tile or w.tile_tokens
+        S = self.num_slots(tile)
+        B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+        po = torch.full((B, Hq, S, D), float("nan"), device=DEV)
+        pl = torch.full((B, Hq, S), float("nan"), device=DEV)
+        o = torch.full((B, Hq, D), float("nan"), device=DEV)
+        l = torch.full((B, Hq), float("nan"), device=DEV)
+        ws_bytes = pkv.decode_workspace_bytes(B, Hq, S * tile, tile, D, 0, split)
+        ws = torch.zeros(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+        pkv.decode_attention_merged(self.pool, layer, self.q[layer], self.dev_table, self.dev_ctx,
+                                    S * tile, tile, w.scale, po, pl, o, l, workspace=ws,
+                                    split_tokens=split)
+        torch.cuda.synchronize()
+        return po, pl, o, l
+
     def decode_rows(self, layer, row_tiles, max_tiles, max_row_tile=None):
         """Per-request tiles (row_tiles [B] on the host, copied to the
         device), then the merge.  Returns torch (part_o, part_lse, out, lse)."""

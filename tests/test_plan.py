@@ -140,3 +140,30 @@ def test_rows_arguments_are_refused_on_the_host(kw, code, needle):
 
 def test_rows_with_no_requests_do_nothing():
     assert rows_raw(FakePool(64), batch=0)[0] == 0
+
+
+def merged_raw(pool, **kw):
+    a = dict(layer=0, q=1 << 20, table=1 << 21, pt_stride=64, ctx=1 << 22, batch=1, hq=24,
+             count=4096, tile=1024, scale=0.0625, po=1 << 23, pl=1 << 24, slots=4,
+             out=1 << 27, lse=1 << 28, ws=1 << 25, ws_bytes=1 << 30, kernel=0, split=0,
+             slot_offset=0)
+    a.update(kw)
+    o = pkv.DecodeOpts(a["kernel"], a["split"], a["slot_offset"])
+    rc = pkv.lib().pkv_decode_attention_merged(
+        pool.handle, a["layer"], a["q"], a["table"], a["pt_stride"], a["ctx"], a["batch"], a["hq"],
+        a["count"], a["tile"], a["scale"], a["po"], a["pl"], a["slots"], a["out"], a["lse"],
+        a["ws"], a["ws_bytes"], ctypes.byref(o), None)
+    return rc, err()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(slots=5), "every slot"),
+    (dict(slot_offset=1, slots=5), "every slot"),
+    (dict(out=0), "NULL"),
+    (dict(lse=0), "NULL"),
+    (dict(out=(1 << 27) + 4), "aligned"),
+    (dict(tile=1000), "tile_tokens"),
+])
+def test_merged_arguments_are_refused_on_the_host(kw, needle):
+    rc, msg = merged_raw(FakePool(64), **kw)
+    assert rc == -1 and needle in msg, msg
