@@ -262,6 +262,41 @@ int pkv_decode_attention_merged(const pkv_pool* pool, int32_t layer, const void*
                                 float* lse, void* workspace, uint64_t workspace_bytes,
                                 const pkv_decode_opts* opts, void* stream);
 
+/* ---------------------------------------------------- runs in one launch --
+ * The runs of two representations (KV-cache engineering, section "Exact
+ * recent pages, compact older pages": a compact older run and an exact
+ * recent run, each with its own pages) decoded by one launch: every run's
+ * tiles are exactly the partials pkv_decode_attention writes for that run
+ * alone (token_begin 0, one work-group per tile, opts.slot_offset =
+ * slot_offset), bit for bit, but the runs' work-groups share one grid, so
+ * neither run waits for the other's last work-group and the launch has one
+ * ramp and one drain.  Then pkv_merge_partials over all slots, as for
+ * separate calls.
+ *   runs[k].pool           bf16 or compact (E4M3) pool; every run's pool has
+ *                          the same KV heads, and layer is valid in each.
+ *   runs[k].dev_table,     the run's own rows (entry i = page i of the run)
+ *   pt_stride, dev_ctx_lens  and lengths, device int32.
+ *   runs[k].token_count    a multiple of tile_tokens, pt_stride * 64 or less.
+ *   runs[k].tile_tokens    multiple of 64 in 64..16384 (a tile is one
+ *                          work-group's split).
+ *   runs[k].slot_offset    first slot of the run; the runs' slot ranges
+ *                          must not overlap and must fit num_slots.
+ * n_runs 1 or 2; the query group must be one the MFMA kernel is built for
+ * (1..8, 12, 16).  Other arguments as pkv_decode_attention. */
+typedef struct pkv_decode_run {
+  const pkv_pool* pool;
+  const int32_t* dev_table;
+  int32_t pt_stride;
+  const int32_t* dev_ctx_lens;
+  int32_t token_count;
+  int32_t tile_tokens;
+  int32_t slot_offset;
+} pkv_decode_run;
+
+int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batch, int32_t num_q_heads,
+                              const pkv_decode_run* runs, int32_t n_runs, float scale,
+                              float* part_out, float* part_lse, int32_t num_slots, void* stream);
+
 /* ------------------------------------------------ per-request tiles --
  * Tiles of their own length for each request of a batch (the same per-tile
  * partials and merge as above; the KV-cache engineering page, section

@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 PROBE = os.path.join(HERE, "probe_read")          # HBM read-ceiling probe (an executable)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "stager.cpp", "admit.cpp", "merge.hip", "decode_valu.hip", "decode_mfma.hip", "append.hip", "compact.hip", "decode_fp8.hip"]
+SOURCES = ["api.cpp", "stager.cpp", "admit.cpp", "merge.hip", "decode_valu.hip", "decode_mfma.hip", "append.hip", "compact.hip", "decode_fp8.hip", "decode_runs.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

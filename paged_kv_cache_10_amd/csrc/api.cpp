@@ -530,6 +530,127 @@ PKV_API int pkv_decode_attention_merged(const pkv_pool* pool, int32_t layer, con
                      workspace_bytes, opts, stream, out, lse);
 }
 
+PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batch,
+                                      int32_t num_q_heads, const pkv_decode_run* runs,
+                                      int32_t n_runs, float scale, float* part_out,
+                                      float* part_lse, int32_t num_slots, void* stream) {
+  if (n_runs < 1 || n_runs > 2) return fail(PKV_ERR_INVALID_ARG, "n_runs = %d, need 1 or 2", n_runs);
+  if (!runs) return fail(PKV_ERR_INVALID_ARG, "runs is NULL");
+  if (batch < 0 || batch > 65535) return fail(PKV_ERR_INVALID_ARG, "batch = %d outside 0..65535", batch);
+  if (num_slots < 1 || num_slots > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "num_slots = %d outside 1..65535", num_slots);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  pkv::RunsArgs r;
+  std::memset(&r, 0, sizeof(r));
+  r.n_runs = n_runs;
+  r.batch = batch;
+  int group = 0;
+  int lo[2] = {0, 0}, hi[2] = {0, 0};          // slots [lo, hi) of each run
+  for (int k = 0; k < n_runs; ++k) {
+    const pkv_decode_run& u = runs[k];
+    if (!u.pool) return fail(PKV_ERR_INVALID_ARG, "runs[%d].pool is NULL", k);
+    const pkv_pool* pool = u.pool;
+    const pkv_geom& G = pool->geom;
+    if (layer < 0 || layer >= G.num_layers)
+      return fail(PKV_ERR_INVALID_ARG, "layer = %d outside 0..%d of runs[%d].pool", layer,
+                  G.num_layers - 1, k);
+    if (k == 0) {
+      r.num_kv_heads = G.num_kv_heads;
+      if (num_q_heads < 1 || num_q_heads % G.num_kv_heads)
+        return fail(PKV_ERR_GEOMETRY,
+                    "num_q_heads = %d must be a positive multiple of num_kv_heads = %d",
+                    num_q_heads, G.num_kv_heads);
+      group = num_q_heads / G.num_kv_heads;
+      int kernel = 0;
+      if (int rc = kernel_for(nullptr, group, &kernel)) return rc;
+    } else if (G.num_kv_heads != r.num_kv_heads) {
+      return fail(PKV_ERR_GEOMETRY, "runs[1].pool has %d KV heads, runs[0].pool %d",
+                  G.num_kv_heads, r.num_kv_heads);
+    }
+    if (u.tile_tokens < G.page_tokens || u.tile_tokens > kMaxMfmaSplit ||
+        u.tile_tokens % G.page_tokens)
+      return fail(PKV_ERR_INVALID_ARG, "runs[%d].tile_tokens = %d must be a multiple of %d in %d..%d",
+                  k, u.tile_tokens, G.page_tokens, G.page_tokens, kMaxMfmaSplit);
+    if (u.token_count < 0 || u.token_count % u.tile_tokens)
+      return fail(PKV_ERR_INVALID_ARG,
+                  "runs[%d].token_count = %d must be a non-negative multiple of its tile_tokens",
+                  k, u.token_count);
+    if ((int64_t)u.pt_stride * G.page_tokens < u.token_count)
+      return fail(PKV_ERR_INVALID_ARG, "runs[%d].pt_stride = %d covers less than token_count = %d",
+                  k, u.pt_stride, u.token_count);
+    const int n_tiles = u.token_count / u.tile_tokens;
+    if (u.slot_offset < 0 || (int64_t)u.slot_offset + n_tiles > num_slots)
+      return fail(PKV_ERR_INVALID_ARG, "runs[%d] slots %d..%d exceed num_slots = %d", k,
+                  u.slot_offset, u.slot_offset + n_tiles - 1, num_slots);
+    lo[k] = u.slot_offset;
+    hi[k] = u.slot_offset + n_tiles;
+    if (batch > 0 && n_tiles > 0 && (!u.dev_table || !u.dev_ctx_lens))
+      return fail(PKV_ERR_INVALID_ARG, "runs[%d].dev_table or dev_ctx_lens is NULL", k);
+    const int64_t wgs = (int64_t)n_tiles * G.num_kv_heads * batch;
+    if (wgs > INT32_MAX / 2)
+      return fail(PKV_ERR_INVALID_ARG, "runs[%d] holds %lld work-groups, more than %d", k,
+                  (long long)wgs, INT32_MAX / 2);
+    r.compact[k] = pool->format == PKV_FORMAT_E4M3;
+    r.n_split[k] = n_tiles;
+    r.wgs[k] = (int32_t)wgs;
+    pkv::DecodeArgs& a = r.e[k];
+    a.arena = static_cast<const uint16_t*>(pool->base);
+    a.page_elems = (int64_t)(pool->page_layer_bytes / 2);
+    a.layer_off = (int64_t)(pool->page_layer_bytes / 2) * pool->num_pages * layer;
+    a.num_pages = (int32_t)pool->num_pages;
+    a.num_kv_heads = G.num_kv_heads;
+    a.q = static_cast<const uint16_t*>(q);
+    a.table = u.dev_table;
+    a.pt_stride = u.pt_stride;
+    a.ctx_lens = u.dev_ctx_lens;
+    a.num_q_heads = num_q_heads;
+    a.token_begin = 0;
+    a.token_count = u.token_count;
+    a.split_tokens = u.tile_tokens;
+    a.row_split = nullptr;
+    a.scale_log2 = scale * pkv::kLog2e;
+    a.out_o = part_out;
+    a.out_lse = part_lse;
+    a.out_slots = num_slots;
+    a.out_slot0 = u.slot_offset;
+    if (r.compact[k]) {
+      pkv::CompactDecodeArgs& c = r.c[k];
+      c.codes = static_cast<const uint8_t*>(pool->base);
+      c.scales = reinterpret_cast<const float*>(static_cast<const char*>(pool->base) +
+                                                pool->scale_offset);
+      c.page_bytes = (int64_t)pool->page_layer_bytes;
+      c.layer_off = (int64_t)pool->page_layer_bytes * pool->num_pages * layer;
+      c.scale_layer_off = (int64_t)2 * G.num_kv_heads * pool->num_pages * layer;
+      c.num_pages = a.num_pages;
+      c.num_kv_heads = a.num_kv_heads;
+      c.q = a.q;
+      c.table = a.table;
+      c.pt_stride = a.pt_stride;
+      c.ctx_lens = a.ctx_lens;
+      c.num_q_heads = a.num_q_heads;
+      c.token_begin = 0;
+      c.token_count = a.token_count;
+      c.split_tokens = a.split_tokens;
+      c.scale_log2 = a.scale_log2;
+      c.out_o = part_out;
+      c.out_lse = part_lse;
+      c.out_slots = num_slots;
+      c.out_slot0 = a.out_slot0;
+    }
+  }
+  if (n_runs == 2 && lo[0] < hi[1] && lo[1] < hi[0])
+    return fail(PKV_ERR_INVALID_ARG, "the runs' slots %d..%d and %d..%d overlap", lo[0], hi[0] - 1,
+                lo[1], hi[1] - 1);
+  if (batch == 0 || r.wgs[0] + (n_runs > 1 ? r.wgs[1] : 0) == 0) return ok();
+  if (!q || !part_out || !part_lse)
+    return fail(PKV_ERR_INVALID_ARG, "q, part_out or part_lse is NULL");
+  if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(part_out) % 16)
+    return fail(PKV_ERR_INVALID_ARG, "q and part_out must be 16-byte aligned");
+  hipError_t e = pkv::launch_decode_runs(r, group, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 PKV_API int pkv_plan_tiles(const int32_t* host_ctx_lens, int32_t batch, int32_t num_kv_heads,
                            int32_t work_groups, int32_t max_tile_tokens,
                            int32_t* host_row_tile_tokens, int32_t* max_tiles_out) {

@@ -109,4 +109,23 @@ struct CrcArgs {
 
 hipError_t launch_crc(const CrcArgs& a, hipStream_t stream);
 
+// Runs of the history decoded in one launch (KV-cache engineering, section
+// "Exact recent pages, compact older pages": runs of two representations).
+// Run k has wgs[k] work-groups (its splits x KV heads x requests, one split
+// per tile) and is read from a compact pool (compact[k] != 0, c[k]) or an
+// exact one (e[k]); the launch's linear work-group ids list run 0's, then
+// run 1's, each run in its own work order.
+struct RunsArgs {
+  int32_t n_runs;              // 1 or 2
+  int32_t compact[2];
+  int32_t n_split[2];          // splits per row of each run
+  int32_t wgs[2];
+  int32_t num_kv_heads;
+  int32_t batch;
+  DecodeArgs e[2];
+  CompactDecodeArgs c[2];
+};
+
+hipError_t launch_decode_runs(const RunsArgs& a, int group, hipStream_t stream);
+
 }  // namespace pkv

@@ -36,7 +36,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int PT = kPageTokens;
 
-  const WorkItem item = dense_item(a.ctx_lens, nullptr, a.token_begin, a.token_count, a.split_tokens);
+  const WorkItem item = dense_item_grid(a.ctx_lens, nullptr, a.token_begin, a.token_count,
+                                        a.split_tokens);
   const int split = item.split;
   const int g = item.g;
   const int b = item.b;

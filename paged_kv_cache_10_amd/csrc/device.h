@@ -107,15 +107,12 @@ __device__ __forceinline__ WorkItem item_at(int b, unsigned j, unsigned ph, unsi
 // row_split (or null) gives each request its own split length; a request
 // needing more splits than the grid row holds gets the row's splits (the
 // kernel flags the uncovered rest).
+// The launch (or the run of a launch) has n_split splits per row, hkv KV
+// heads and batch requests; lin is the work-group's linear id within it.
 __device__ __forceinline__ WorkItem dense_item(const int32_t* ctx_lens, const int32_t* row_split,
                                                int token_begin, int token_count,
-                                               int split_tokens) {
-  // grid sizes and ids are uniform: readfirstlane keeps the walk below
-  // (and its loads) on the scalar unit
-  const unsigned n_split = __builtin_amdgcn_readfirstlane(gridDim.x);
-  const unsigned hkv = __builtin_amdgcn_readfirstlane(gridDim.y);
-  const int batch = __builtin_amdgcn_readfirstlane(gridDim.z);
-  const unsigned lin = blockIdx.x + n_split * (blockIdx.y + hkv * blockIdx.z);
+                                               int split_tokens, unsigned n_split, unsigned hkv,
+                                               int batch, unsigned lin) {
   // live splits of a request; a malformed per-request split reads nothing
   auto live_of = [&](int ctx, int S) {
     return S >= kPageTokens ? min(live_splits(ctx, token_begin, token_count, S), (int)n_split) : 0;
@@ -173,6 +170,20 @@ __device__ __forceinline__ WorkItem dense_item(const int32_t* ctx_lens, const in
   }
   WorkItem none = {0, 0, 0, 0, split_tokens};   // not reached: the items cover the grid
   return none;
+}
+
+// The item of a launch whose grid is (splits per row, KV heads, requests).
+__device__ __forceinline__ WorkItem dense_item_grid(const int32_t* ctx_lens,
+                                                    const int32_t* row_split, int token_begin,
+                                                    int token_count, int split_tokens) {
+  // grid sizes and ids are uniform: readfirstlane keeps the walk (and its
+  // loads) on the scalar unit
+  const unsigned n_split = __builtin_amdgcn_readfirstlane(gridDim.x);
+  const unsigned hkv = __builtin_amdgcn_readfirstlane(gridDim.y);
+  const int batch = __builtin_amdgcn_readfirstlane(gridDim.z);
+  const unsigned lin = blockIdx.x + n_split * (blockIdx.y + hkv * blockIdx.z);
+  return dense_item(ctx_lens, row_split, token_begin, token_count, split_tokens, n_split, hkv,
+                    batch, lin);
 }
 
 // ---- Wave-level reductions on the VALU's lane-crossing paths, no LDS round

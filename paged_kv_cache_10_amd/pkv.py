@@ -32,7 +32,7 @@ EXPORTS = [
     "pkv_admit_step", "pkv_admit_get_counts", "pkv_admit_events", "pkv_admit_destroy",
     "pkv_compact_page_bytes", "pkv_compact_pool_create", "pkv_pool_format",
     "pkv_compact_convert", "pkv_compact_crc", "pkv_plan_tiles", "pkv_decode_attention_rows",
-    "pkv_decode_attention_merged",
+    "pkv_decode_attention_merged", "pkv_decode_attention_runs",
 ]
 
 
@@ -50,6 +50,13 @@ class Geom(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("slot_offset", ctypes.c_int32)]
+
+
+class DecodeRun(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_void_p), ("dev_table", ctypes.c_void_p),
+                ("pt_stride", ctypes.c_int32), ("dev_ctx_lens", ctypes.c_void_p),
+                ("token_count", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
                 ("slot_offset", ctypes.c_int32)]
 
 
@@ -117,6 +124,8 @@ def lib():
                                                   ctypes.c_float, P, P, I32, P, P, P, U64,
                                                   ctypes.POINTER(DecodeOpts), P]
         L.pkv_plan_tiles.argtypes = [I32P, I32, I32, I32, I32, I32P, I32P]
+        L.pkv_decode_attention_runs.argtypes = [I32, P, I32, I32, ctypes.POINTER(DecodeRun), I32,
+                                                ctypes.c_float, P, P, I32, P]
         L.pkv_decode_attention_rows.argtypes = [P, I32, P, P, I32, P, I32, I32, P, I32, I32,
                                                 ctypes.c_float, P, P, I32,
                                                 ctypes.POINTER(DecodeOpts), P]
@@ -321,6 +330,29 @@ def decode_attention_merged(pool, layer, q, dev_table, dev_ctx_lens, token_count
         int(tile_tokens), float(scale), _ptr(part_out, torch.float32, "part_out"),
         _ptr(part_lse, torch.float32, "part_lse"), num_slots, _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def decode_attention_runs(layer, q, runs, scale, part_out, part_lse, stream=None):
+    """Runs decoded in one launch.  runs: a list of (pool, dev_table,
+    dev_ctx_lens, token_count, tile_tokens, slot_offset); part_out [B, Hq,
+    num_slots, D], part_lse [B, Hq, num_slots]."""
+    import torch
+    B, Hq, D = q.shape
+    if part_out.dim() != 4 or part_out.shape[:2] != (B, Hq) or part_out.shape[3] != D:
+        raise ValueError("part_out must be [B, Hq, num_slots, D]")
+    num_slots = part_out.shape[2]
+    if tuple(part_lse.shape) != (B, Hq, num_slots):
+        raise ValueError("part_lse must be [B, Hq, num_slots]")
+    arr = (DecodeRun * max(1, len(runs)))()
+    for k, (pool, table, ctx, count, tile, off) in enumerate(runs):
+        if table.dim() != 2 or table.shape[0] != B or table.stride(1) != 1:
+            raise ValueError("each run's table must be [B, pt_stride] with contiguous rows")
+        arr[k] = DecodeRun(pool.handle, table.data_ptr(), int(table.stride(0)),
+                           _ptr(ctx, torch.int32, "dev_ctx_lens"), int(count), int(tile), int(off))
+    _check(lib().pkv_decode_attention_runs(
+        int(layer), _ptr(q, torch.bfloat16, "q"), B, Hq, arr, len(runs), float(scale),
+        _ptr(part_out, torch.float32, "part_out"), _ptr(part_lse, torch.float32, "part_lse"),
+        num_slots, _stream(stream)))
 
 
 def plan_tiles(ctx_lens, num_kv_heads, work_groups=256, max_tile_tokens=16384):

@@ -271,11 +271,14 @@ class Runs:
         etile = etile or tile
         return (max(1, -(-int(self.cctx.max()) // tile)), max(1, -(-int(self.ectx.max()) // etile)))
 
-    def decode(self, layer, tile, split=0, etile=None, esplit=None, tail_stream=False):
+    def decode(self, layer, tile, split=0, etile=None, esplit=None, tail_stream=False,
+               one_launch=False):
         """Compact run with (tile, split), exact run with (etile, esplit),
         defaulting to the same; one merge over both runs' slots.  With
         tail_stream the exact run decodes on a second stream, concurrent
-        with the compact run, and is joined before the merge."""
+        with the compact run, and is joined before the merge; with one_launch
+        both runs are one pkv_decode_attention_runs launch (every tile one
+        split)."""
         w, case = self.w, self.case
         etile = etile or tile
         esplit = split if esplit is None else esplit
@@ -285,6 +288,16 @@ class Runs:
         pl = torch.full((B, Hq, Sc + Se), float("nan"), device=DEV)
         o = torch.empty((B, Hq, D), device=DEV)
         l = torch.empty((B, Hq), device=DEV)
+        if one_launch:
+            assert split in (0, tile) and esplit in (0, etile), "one launch: a tile is a split"
+            pkv.decode_attention_runs(
+                layer, case.q[layer],
+                [(self.pool, self.dev_ct, self.dev_cc, Sc * tile, tile, 0),
+                 (case.pool, self.dev_et, self.dev_ec, Se * etile, etile, Sc)],
+                w.scale, po, pl)
+            pkv.merge_partials(po, pl, o, l)
+            torch.cuda.synchronize()
+            return po, pl, o, l
         nb = max(pkv.decode_workspace_bytes(B, Hq, Sc * tile, tile, D, 0, split),
                  pkv.decode_workspace_bytes(B, Hq, Se * etile, etile, D, 0, esplit))
         ws = torch.zeros(max(nb, 16) // 4 + 4, device=DEV)

@@ -176,6 +176,28 @@ def test_two_runs_with_their_own_tilings(gpu):
     runs.check(got, runs.oracle(0, 3584, etile=512))
 
 
+@pytest.mark.parametrize("boundary", ["all_full_pages", "half", "none"])
+@pytest.mark.parametrize("tile,etile", [(1024, 1024), (4096, 512)])
+def test_two_runs_in_one_launch_equal_two_calls_bitwise(gpu, boundary, tile, etile):
+    """pkv_decode_attention_runs writes the bits of the two separate calls
+    (and so matches the oracle as they do)."""
+    w = I.Workload("cone", seed=67, ctx_lens=RAGGED, num_layers=1, tile_tokens=tile,
+                   arena_pages=900)
+    case = Case(w, fill=I.BF16_QNAN)
+    if boundary == "all_full_pages":
+        c = [n // 64 * 64 for n in w.ctx_lens]
+    elif boundary == "half":
+        c = [n // 128 * 64 for n in w.ctx_lens]
+    else:
+        c = [0] * w.batch
+    runs = Runs(case, c, seed=len(boundary))
+    sep = runs.decode(0, tile, tile, etile, etile)
+    one = runs.decode(0, tile, tile, etile, etile, one_launch=True)
+    for x, y in zip(sep, one):
+        assert same_bits(x, y)
+    runs.check(one, runs.oracle(0, tile, etile=etile))
+
+
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (48, 4), (64, 4), (16, 2)])
 def test_compact_query_group_sizes(gpu, hq, hkv):
     """The compact kernel for query groups of 1, 2, 4, 8, 12 and 16 heads per
@@ -223,11 +245,12 @@ def test_long262k_two_runs_match_oracle(gpu, long_runs, layer):
     from bench import COMPACT_LAUNCH
     cl = COMPACT_LAUNCH["long262k"]
     got = long_runs.decode(layer, cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"],
-                           tail_stream=cl["tail_stream"])
+                           tail_stream=cl["schedule"] == "tail_stream",
+                           one_launch=cl["schedule"] == "one_launch")
     long_runs.check(got, long_runs.oracle(layer, cl["tile"], with_exact=False,
                                           etile=cl["exact_tile"]))
     # the runs write disjoint slots: decoding them one after the other on one
-    # stream gives the same bits
+    # stream, in two calls, gives the same bits
     serial = long_runs.decode(layer, cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"])
     for a, b in zip(got, serial):
         assert torch.equal(a, b)
