@@ -254,3 +254,58 @@ def test_long262k_two_runs_match_oracle(gpu, long_runs, layer):
     serial = long_runs.decode(layer, cl["tile"], cl["split"], cl["exact_tile"], cl["exact_split"])
     for a, b in zip(got, serial):
         assert torch.equal(a, b)
+
+
+def test_runs_of_one_representation_in_one_launch(gpu):
+    """pkv_decode_attention_runs with two exact runs (the history cut at a
+    page boundary, each run with its own table) and with one run: the bits
+    of the separate pkv_decode_attention calls."""
+    w = I.Workload("xruns", seed=68, ctx_lens=[9000, 1500, 0, 4097], num_layers=1,
+                   tile_tokens=1024)
+    case = Case(w, fill=I.BF16_QNAN)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    cut = 4096                                     # run 0: tokens [0, 4096), run 1: the rest
+    c0 = np.minimum(case.ctx, cut).astype(np.int32)
+    c1 = np.maximum(case.ctx - cut, 0).astype(np.int32)
+    t0 = case.table.copy()
+    t0[:, cut // 64:] = -1                         # padding past a run's pages is -1
+    t1 = np.full_like(case.table, -1)
+    t1[:, :case.table.shape[1] - cut // 64] = case.table[:, cut // 64:]
+    t1[c1 == 0] = -1
+    dev = {}
+    for name, tab, ln in (("r0", t0, c0), ("r1", t1, c1)):
+        dt = torch.empty(tab.shape, dtype=torch.int32, device=DEV)
+        dc = torch.empty(B, dtype=torch.int32, device=DEV)
+        pkv.page_table_write(case.pool, tab, ln, dt, dc)
+        dev[name] = (dt, dc)
+    S0, S1 = cut // 1024, -(-int(c1.max()) // 512)
+    q = case.q[0]
+
+    def fresh():
+        return (torch.full((B, Hq, S0 + S1, D), float("nan"), device=DEV),
+                torch.full((B, Hq, S0 + S1), float("nan"), device=DEV))
+    po, pl = fresh()
+    pkv.decode_attention(case.pool, 0, q, dev["r0"][0], dev["r0"][1], 0, S0 * 1024, 1024, w.scale,
+                         po, pl, split_tokens=1024)
+    pkv.decode_attention(case.pool, 0, q, dev["r1"][0], dev["r1"][1], 0, S1 * 512, 512, w.scale,
+                         po, pl, split_tokens=512, slot_offset=S0)
+    po2, pl2 = fresh()
+    pkv.decode_attention_runs(0, q, [(case.pool, dev["r0"][0], dev["r0"][1], S0 * 1024, 1024, 0),
+                                     (case.pool, dev["r1"][0], dev["r1"][1], S1 * 512, 512, S0)],
+                              w.scale, po2, pl2)
+    torch.cuda.synchronize()
+    assert same_bits(po, po2) and same_bits(pl, pl2)
+    # the merged result is the softmax over the whole history
+    o = torch.empty((B, Hq, D), device=DEV)
+    l = torch.empty((B, Hq), device=DEV)
+    pkv.merge_partials(po2, pl2, o, l)
+    ref = case.oracle_layer(0)
+    for b in range(B):
+        assert_out_close(o[b].cpu().numpy(), ref[b][2])
+        assert_lse_close(l[b].cpu().numpy(), ref[b][3])
+    # one run alone: the bits of its own call
+    po3, pl3 = fresh()
+    pkv.decode_attention_runs(0, q, [(case.pool, dev["r0"][0], dev["r0"][1], S0 * 1024, 1024, 0)],
+                              w.scale, po3, pl3)
+    torch.cuda.synchronize()
+    assert same_bits(po3[:, :, :S0], po[:, :, :S0]) and same_bits(pl3[:, :, :S0], pl[:, :, :S0])
