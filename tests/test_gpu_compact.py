@@ -198,9 +198,10 @@ def test_two_runs_in_one_launch_equal_two_calls_bitwise(gpu, boundary, tile, eti
     runs.check(one, runs.oracle(0, tile, etile=etile))
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (48, 4), (64, 4), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (12, 4), (16, 4), (20, 4), (28, 4), (32, 4),
+                                    (48, 4), (64, 4), (16, 2)])
 def test_compact_query_group_sizes(gpu, hq, hkv):
-    """The compact kernel for query groups of 1, 2, 4, 8, 12 and 16 heads per
+    """The compact kernel for query groups of 1, 2, 3, 4, 5, 7, 8, 12 and 16 heads per
     KV head, lengths around page edges (every full page compact, the partial
     last page exact), poisoned exact padding."""
     w = I.Workload("cgroups", seed=66, ctx_lens=[130, 2049, 777], num_layers=1,

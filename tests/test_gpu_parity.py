@@ -176,9 +176,10 @@ def test_workspace_reuse_across_calls(ragged, kernel):
         assert same_bits(po, ref[0]) and same_bits(pl, ref[1])
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (48, 4), (64, 4), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (12, 4), (16, 4), (20, 4), (28, 4), (32, 4),
+                                    (48, 4), (64, 4), (16, 2)])
 def test_query_group_sizes(gpu, hq, hkv):
-    """Query groups of 1, 2, 4, 8, 12 and 16 heads per KV head (MFMA; the
+    """Query groups of 1, 2, 3, 4, 5, 7, 8, 12 and 16 heads per KV head (MFMA; the
     VALU kernel up to 8), against the oracle, lengths around page edges."""
     w = I.Workload("groups", seed=21, ctx_lens=[130, 2049, 777], num_layers=1,
                    tile_tokens=1024, num_q_heads=hq, num_kv_heads=hkv)
