@@ -2,7 +2,9 @@
 
     python -m paged_kv_cache_10_amd.build [--resource-usage]
 
-Also builds ``probe_read``, a standalone HBM read-ceiling probe.
+Also builds ``probe_read``, a standalone HBM read-ceiling probe, and
+``tests/c_abi/decode_from_c``, the test program that drives the C ABI from
+C++ alone.
 Every source is compiled by hipcc with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``), objects go to
 ``_build/`` and the shared library lands next to this file.
@@ -20,6 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 PROBE = os.path.join(HERE, "probe_read")          # HBM read-ceiling probe (an executable)
+C_ABI_SRC = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "decode_from_c.cpp")
+C_ABI_EXE = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "decode_from_c")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "stager.cpp", "admit.cpp", "merge.hip", "decode_valu.hip", "decode_mfma.hip", "append.hip", "compact.hip", "decode_fp8.hip", "decode_runs.hip"]
@@ -74,6 +78,14 @@ def build(resource_usage=False, verbose=False):
     if p.returncode != 0:
         raise RuntimeError(f"probe build failed:\n{p.stdout}{p.stderr}")
     os.replace(PROBE + ".tmp", PROBE)
+    # the C-ABI test program (tests/c_abi): the library used from C++ alone
+    cmd = [hipcc(), "-O2", "-std=c++17", f"--offload-arch={ARCH}", "-x", "hip", C_ABI_SRC,
+           "-o", C_ABI_EXE + ".tmp", "-L", HERE, "-lpkv",
+           "-Wl,-rpath,$ORIGIN/../../paged_kv_cache_10_amd"]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"C-ABI test program build failed:\n{p.stdout}{p.stderr}")
+    os.replace(C_ABI_EXE + ".tmp", C_ABI_EXE)
     if verbose or resource_usage:
         for l in logs:
             print(l)
