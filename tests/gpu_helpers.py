@@ -225,7 +225,7 @@ class Runs:
     (whole pages) of every request, converted on the GPU; the exact run's
     table rows start at the first exact page."""
 
-    def __init__(self, case, compact_tokens, seed=0, spare=3):
+    def __init__(self, case, compact_tokens, seed=0, spare=3, stream=None):
         w = self.w = case.w
         self.case = case
         self.c = np.array(compact_tokens, dtype=np.int32)
@@ -254,9 +254,14 @@ class Runs:
         self.src = np.array(src, np.int32)
         self.dst = np.array(dst, np.int32)
         self.crc = torch.zeros(max(total, 1), dtype=torch.int32, device=DEV)
+        # stream: the conversion is queued there and left running (the caller
+        # synchronizes before decoding the compact run)
+        self.src_dev = torch.from_numpy(self.src).to(DEV)
+        self.dst_dev = torch.from_numpy(self.dst).to(DEV)
+        torch.cuda.synchronize()
         if total:
-            pkv.compact_convert(case.pool, self.pool, torch.from_numpy(self.src).to(DEV),
-                                torch.from_numpy(self.dst).to(DEV), self.crc[:total])
+            pkv.compact_convert(case.pool, self.pool, self.src_dev, self.dst_dev,
+                                self.crc[:total], stream=stream)
         self.cctx = self.c.copy()
         self.ectx = (np.array(w.ctx_lens, np.int32) - self.c).astype(np.int32)
         self.dev_ct = torch.empty(self.ctable.shape, dtype=torch.int32, device=DEV)
@@ -265,7 +270,8 @@ class Runs:
         self.dev_ec = torch.empty(w.batch, dtype=torch.int32, device=DEV)
         pkv.page_table_write(self.pool, self.ctable, self.cctx, self.dev_ct, self.dev_cc)
         pkv.page_table_write(case.pool, self.etable, self.ectx, self.dev_et, self.dev_ec)
-        torch.cuda.synchronize()
+        if stream is None:
+            torch.cuda.synchronize()
 
     def slots(self, tile, etile=None):
         etile = etile or tile

@@ -310,3 +310,30 @@ def test_runs_of_one_representation_in_one_launch(gpu):
                               w.scale, po3, pl3)
     torch.cuda.synchronize()
     assert same_bits(po3[:, :, :S0], po[:, :, :S0]) and same_bits(pl3[:, :, :S0], pl[:, :, :S0])
+
+
+def test_background_conversion_then_publish(gpu):
+    """The pages' lifecycle: conversion and CRC run on their own stream while
+    exact decode steps go on (their bits unchanged); once the CRC checks,
+    the tables switch to the compact run (publish) and the two-run decode
+    matches the oracle on the dequantised history."""
+    w = I.Workload("cbg", seed=69, ctx_lens=[20000, 9000, 4100], num_layers=2, tile_tokens=2048,
+                   arena_pages=600)
+    case = Case(w, fill=I.BF16_QNAN)
+    ref = [case.decode(layer, tile=2048, split=2048) for layer in range(2)]
+    side = torch.cuda.Stream()                     # default priority
+    runs = Runs(case, [n // 2048 * 2048 for n in w.ctx_lens], stream=side)
+    for _ in range(3):                             # decode steps beside the conversion
+        for layer in range(2):
+            got = case.decode(layer, tile=2048, split=2048)
+            for x, y in zip(got, ref[layer]):
+                assert same_bits(x, y)
+    side.synchronize()
+    total = runs.src.size
+    again = torch.empty(total, dtype=torch.int32, device=DEV)
+    pkv.compact_crc(runs.pool, runs.dst_dev, again)
+    torch.cuda.synchronize()
+    assert torch.equal(again, runs.crc[:total])     # the published pages are the converted ones
+    for layer in range(2):
+        got = runs.decode(layer, 2048, 2048, 1024, 1024, one_launch=True)
+        runs.check(got, runs.oracle(layer, 2048, etile=1024))
