@@ -189,7 +189,9 @@ def main():
             or args.compact_older):
         plan = 0
     w.tile_tokens = args.tile or launch.get("tile", w.tile_tokens)
-    args.split = args.split or launch.get("split", 0)
+    # a 32,768-token window decoded alone holds 1/8 of the history: 512-token
+    # splits give its launch 256 work-groups (4,096-token ones only 32)
+    args.split = args.split or (512 if args.staged else launch.get("split", 0))
     overlap = args.overlap and not args.serial
     T = w.tile_tokens
     B, Hq, Hkv, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
