@@ -99,59 +99,86 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 // whose log-sum-exps sit in the lanes (lv at lane u = slot u) and whose
 // outputs are in LDS (win[u][lane]): merge_slots' arithmetic (the same max,
 // the same exp per slot, the slots summed in increasing order), so a group
-// merged here has the bits merge_slots gives it.
+// merged here has the bits merge_slots gives it.  The outputs are read
+// eight slots at a time, so the LDS reads of a batch are in flight together.
 __device__ __forceinline__ Merged merge_window(float lv, int lo, int cnt, int lane,
                                                const float2 (*win)[kMergeThreads]) {
-  const bool mine = lane >= lo && lane < lo + cnt;
+  constexpr int kBatch = 8;
+  const int hi = lo + cnt;
+  const bool mine = lane >= lo && lane < hi;
   const float m = wave_max_nan(mine ? lv : -INFINITY);
   if (m == -INFINITY) return Merged{make_float2(0.f, 0.f), -INFINITY};   // every slot empty
   const float wl = mine ? expf(lv - m) : 0.f;
   float2 acc = make_float2(0.f, 0.f);
   float wsum = 0.f;
-  for (int u = lo; u < lo + cnt; ++u) {
-    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
-    if (w != 0.f) {                            // uniform: 0 for an empty slot
-      const float2 ou = win[u][lane];
-      acc.x = fmaf(w, ou.x, acc.x);
-      acc.y = fmaf(w, ou.y, acc.y);
-      wsum += w;
+  for (int u0 = lo; u0 < hi; u0 += kBatch) {
+    float2 ou[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      ou[i] = (u0 + i < hi) ? win[u0 + i][lane] : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (u0 + i < hi) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u0 + i));
+        if (w != 0.f) {                        // uniform: 0 for an empty slot
+          acc.x = fmaf(w, ou[i].x, acc.x);
+          acc.y = fmaf(w, ou[i].y, acc.y);
+          wsum += w;
+        }
+      }
     }
   }
   return Merged{make_float2(acc.x / wsum, acc.y / wsum), m + logf(wsum)};
 }
 
 // Tile finalize and final merge in one launch, for rows of at most 64 split
-// partials: all of a row's split partials are loaded at once (into LDS),
-// every group j is merged into output slot j (as merge_kernel would), and
-// the group results, kept in LDS and in lane j, are merged again into
-// fin_o / fin_lse (as merge_kernel over those slots would), so the bits
-// equal the two launches'.
-__global__ __launch_bounds__(kMergeThreads) void merge2_kernel(MergeArgs a, float* fin_o,
-                                                                float* fin_lse) {
-  const int row = blockIdx.x, part = blockIdx.z, lane = threadIdx.x;
+// partials.  Four waves share one (row, 128-channel half): together they
+// load all of the row's split partials into LDS (slot u by wave u % 4, so
+// every load is in flight at once), wave w then merges groups j = w, w + 4,
+// ... into output slot j (as merge_kernel would), and wave 0 merges the
+// group results, kept in LDS, into fin_o / fin_lse (as merge_kernel over
+// those slots would), so the bits equal the two launches'.
+constexpr int kMerge2Waves = 4;
+
+__global__ __launch_bounds__(kMergeThreads * kMerge2Waves) void merge2_kernel(MergeArgs a,
+                                                                               float* fin_o,
+                                                                               float* fin_lse) {
+  constexpr int kPerWave = kMergeChunk / kMerge2Waves;
+  const int row = blockIdx.x, part = blockIdx.z;
+  const int w = threadIdx.x / kMergeThreads, lane = threadIdx.x % kMergeThreads;
   __shared__ float2 split_o[kMergeChunk][kMergeThreads];
   __shared__ float2 tile_o[kMergeChunk][kMergeThreads];
+  __shared__ float tile_lse[kMergeChunk];
   const float* lse_in = a.in_lse + (int64_t)row * a.in_slots;
   const float2* o_in = reinterpret_cast<const float2*>(
       a.in_o + (int64_t)row * a.in_slots * kHeadDim + 128 * part) + lane;
   {
-    float2 o[kMergeChunk];
-    load_chunk(o, o_in, a.in_slots);
+    float2 o[kPerWave];
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u)
-      if (u < a.in_slots) split_o[u][lane] = o[u];
+    for (int i = 0; i < kPerWave; ++i) {
+      const int u = kMerge2Waves * i + w;
+      o[i] = (u < a.in_slots) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int u = kMerge2Waves * i + w;
+      if (u < a.in_slots) split_o[u][lane] = o[i];
+    }
   }
   const float lv = (lane < a.in_slots) ? lse_in[lane] : -INFINITY;
-  float tl = -INFINITY;                        // lane j: the log-sum-exp of group j
-  for (int j = 0; j < a.n_out; ++j) {
+  __syncthreads();
+  for (int j = w; j < a.n_out; j += kMerge2Waves) {
     const int lo = j * a.group;
     const Merged r = merge_window(lv, lo, min(a.group, a.in_slots - lo), lane, split_o);
     const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
     reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part)[lane] = r.o;
     if (part == 0 && lane == 0) a.out_lse[orow] = r.lse;
     tile_o[j][lane] = r.o;
-    if (lane == j) tl = r.lse;
+    if (lane == 0) tile_lse[j] = r.lse;
   }
+  __syncthreads();
+  if (w != 0) return;
+  const float tl = (lane < a.n_out) ? tile_lse[lane] : -INFINITY;   // lane j: group j's
   const Merged r = merge_window(tl, 0, a.n_out, lane, tile_o);
   reinterpret_cast<float2*>(fin_o + (int64_t)row * kHeadDim + 128 * part)[lane] = r.o;
   if (part == 0 && lane == 0) fin_lse[row] = r.lse;
@@ -171,7 +198,8 @@ hipError_t launch_merge2(const MergeArgs& a, int rows, float* fin_o, float* fin_
   if (rows <= 0 || a.n_out <= 0) return hipSuccess;
   if (a.in_slots > kMergeChunk) return hipErrorInvalidValue;   // one window per row
   dim3 grid(rows, 1, kMergeParts);
-  hipLaunchKernelGGL(merge2_kernel, grid, dim3(kMergeThreads), 0, stream, a, fin_o, fin_lse);
+  hipLaunchKernelGGL(merge2_kernel, grid, dim3(kMergeThreads * kMerge2Waves), 0, stream, a,
+                     fin_o, fin_lse);
   return hipGetLastError();
 }
 
