@@ -153,6 +153,25 @@ def test_merge_identity_and_empty_insertion_bitwise(stress):
         assert same_bits(x, y)
 
 
+@pytest.mark.parametrize("n", [1, 2, 17, 63, 64])
+def test_merge_of_one_chunk_matches_two_chunks_bitwise(stress, n):
+    """Rows of at most 64 slots are merged as one chunk of slots; the same
+    slots followed by empty ones (more than 64 in all) take a second chunk.
+    Empty slots contribute nothing, so the two must agree bit for bit; both
+    against the float64 merge of the same FP32 partials."""
+    po, pl, _, _ = stress
+    po_n, pl_n = po[:, :, :n].contiguous(), pl[:, :, :n].contiguous()
+    few = merge(po_n, pl_n)
+    pad = 65 - n
+    general = merge(torch.cat([po_n, torch.full_like(po[:, :, :pad], float("nan"))], 2).contiguous(),
+                    torch.cat([pl_n, torch.full_like(pl[:, :, :pad], -math.inf)], 2).contiguous())
+    for x, y in zip(few, general):
+        assert same_bits(x, y)
+    eo, el = oracle.merge(po_n.cpu().numpy(), pl_n.cpu().numpy())
+    assert_out_close(few[0].cpu().numpy(), eo, tol=1e-4)
+    assert_lse_close(few[1].cpu().numpy(), el, tol=1e-4)
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_workspace_reuse_across_calls(ragged, kernel):
     """Tiles of 32 splits (2,048-token tiles of 64-token splits): three
