@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void convert_kernel(ConvertArgs a) {
   float amax = 0.f;
 #pragma unroll
   for (int m = 0; m < kPageTokens * kHeadDim / 8 / 256; ++m) {
-    const uint4 u = blk[tid + 256 * m];
+    const uint4 u = load_stream(blk + tid + 256 * m);
     blk_lds[tid + 256 * m] = u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_elem(u, e)));
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void crc_kernel(CrcArgs a) {
     for (int64_t v0 = 0; v0 < seg / 16; v0 += 8) {     // one 128-byte line at a time
       uint4 line[8];
 #pragma unroll
-      for (int v = 0; v < 8; ++v) line[v] = p[v0 + v];
+      for (int v = 0; v < 8; ++v) line[v] = load_stream(p + v0 + v);
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const uint32_t w[4] = {line[v].x, line[v].y, line[v].z, line[v].w};

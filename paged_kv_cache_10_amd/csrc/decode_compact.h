@@ -67,7 +67,7 @@ struct PageRef {
 __device__ __forceinline__ void load_blk(uint4 (&r)[16], const uint8_t* blk, int lane) {
   const uint4* p = reinterpret_cast<const uint4*>(blk) + lane;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) r[i] = p[i * 64];
+  for (int i = 0; i < 16; ++i) r[i] = load_stream(p + i * 64);
 }
 
 // One page: QK, online softmax, PV.  With kNext the next page's K loads

@@ -78,14 +78,14 @@ __device__ __forceinline__ void load_k(uint4 (&kr)[2][8], const PageRef& pg, int
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) kr[t][kb] = p[(t * 8 + kb) * 64];
+    for (int kb = 0; kb < 8; ++kb) kr[t][kb] = load_stream(p + (t * 8 + kb) * 64);
 }
 
 // V^T operand of a 32-token chunk: channel block db at piece db*64 + lane.
 __device__ __forceinline__ void load_v(uint4 (&vr)[16], const PageRef& pg, int base, int lane) {
   const uint4* p = reinterpret_cast<const uint4*>(pg.v) + (base >> 5) * 1024 + lane;
 #pragma unroll
-  for (int db = 0; db < 16; ++db) vr[db] = p[db * 64];
+  for (int db = 0; db < 16; ++db) vr[db] = load_stream(p + db * 64);
 }
 
 // One 32-token chunk: QK, online softmax, PV.  `live` = tokens of the chunk

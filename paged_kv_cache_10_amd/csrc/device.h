@@ -27,6 +27,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // 2^x on the transcendental unit; 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte load marked nontemporal (the instruction's nt bit): the history
+// is read once per step, so its lines are streamed past the caches instead
+// of being allocated in them.  Measured on the decode kernels' access shape
+// (random 32 KiB blocks, one 4-wave work-group per CU): 6.78-6.83 TB/s
+// against 6.00-6.02 TB/s for ordinary loads.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float2 load_stream(const float2* p) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+  return make_float2(v.x, v.y);
+}
+
 // Pool block layout.  A (layer, page, K|V, kv head) block holds 64 tokens x
 // 256 channels as 2,048 pieces of 16 bytes (8 bf16), stored in the order the
 // MFMA kernel's wave loads consume them: 64 consecutive pieces (1 KiB) per

@@ -36,7 +36,7 @@ struct Merged {
 __device__ __forceinline__ void load_chunk(float2 (&o)[kMergeChunk], const float2* o_in, int n) {
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u)
-    o[u] = (u < n) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
+    o[u] = (u < n) ? load_stream(o_in + (int64_t)u * (kHeadDim / 2)) : make_float2(0.f, 0.f);
 }
 
 // The merge of cnt slots: lv = this lane's slot's log-sum-exp (lane < cnt,
@@ -157,7 +157,8 @@ __global__ __launch_bounds__(kMergeThreads * kMerge2Waves) void merge2_kernel(Me
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int u = kMerge2Waves * i + w;
-      o[i] = (u < a.in_slots) ? o_in[(int64_t)u * (kHeadDim / 2)] : make_float2(0.f, 0.f);
+      o[i] = (u < a.in_slots) ? load_stream(o_in + (int64_t)u * (kHeadDim / 2))
+                              : make_float2(0.f, 0.f);
     }
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
