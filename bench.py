@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "30b4aefdc4cfc4ba3463fec16a60efda70e4c863ed7d750d775f14dfea240c94",
+    "source_sha256": "b04ff7e6ad37e97da8cbc69fbc98181856bc276c36435816aeacf2bbe0a856ae",
     "workload": "long262k", "tile": 4096, "split": 4096,
     "fetch_kib": 524499.8, "fetch_scale": 1048576 / 524300.1,
     "write_kib": 1584.0, "write_scale": 1.0,
@@ -49,9 +49,9 @@ KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "c108c25dd29a8764d4178e9deb001cd7a572a9fca84241420a4f9e2dfd85bf01",
+    "source_sha256": "81e902467739c7a54d0883608d22293b7bc6a68415ab5abe8a33893c8ab7faeb",
     "workload": "long262k", "tile": 4800, "split": 4800,
-    "fetch_kib": 230085.4, "fetch_scale": 1048576 / 524299.8,
+    "fetch_kib": 230053.1, "fetch_scale": 1048576 / 524299.5,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_amd/csrc/decode_compact.h",
@@ -59,10 +59,10 @@ FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_a
 
 # The same for the one-launch kernel of both runs (COMPACT_LAUNCH, "one_launch").
 PMC_TRAFFIC_RUNS = {
-    "source_sha256": "89562be8926aa6785531d43b93bc46a6322ba320fd97bd0e41af1ffec1cfe0ad",
+    "source_sha256": "750bf3dfc1a6c74e0e8b15432ee2377b07373bdb310bfc2373fcf1ebe4f2be1d",
     "workload": "long262k", "tile": 4800, "exact_tile": 2048,
-    "fetch_kib": 295781.4, "fetch_scale": 1048576 / 524299.8,
-    "write_kib": 1586.2, "write_scale": 1.0,
+    "fetch_kib": 295727.6, "fetch_scale": 1048576 / 524299.5,
+    "write_kib": 1584.1, "write_scale": 1.0,
 }
 RUNS_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_runs.hip", "paged_kv_cache_10_amd/csrc/decode_compact.h",
                 "paged_kv_cache_10_amd/csrc/decode_exact.h", "paged_kv_cache_10_amd/csrc/compact.h",
@@ -350,7 +350,7 @@ def main():
         if ceiling is not None:
             res["read_ceiling"] = ceiling
             res["roofline"]["frac_of_measured_ceiling"] = round(
-                res["roofline"]["achieved"] / ceiling["blocks_GBs"], 4)
+                res["roofline"]["achieved"] / ceiling["blocks_nt_GBs"], 4)
         if args.copy_probe:
             res["copy_probe"] = copy_probe(dev, stream)
         print(json.dumps(res), flush=True)
@@ -422,7 +422,7 @@ def main():
 
     if ceiling is not None:
         res["read_ceiling"] = ceiling
-        res["roofline"]["frac_of_measured_ceiling"] = round(dec_gbs / ceiling["blocks_GBs"], 4)
+        res["roofline"]["frac_of_measured_ceiling"] = round(dec_gbs / ceiling["blocks_nt_GBs"], 4)
 
     if args.copy_probe:
         res["copy_probe"] = copy_probe(dev, stream)

@@ -155,10 +155,12 @@ __global__ __launch_bounds__(256) void crc_kernel(CrcArgs a) {
     const uint4* p = reinterpret_cast<const uint4*>(
         a.codes + ((int64_t)l * a.num_pages + pg) * a.page_bytes + (int64_t)tid * seg);
     uint32_t c = 0u;
+    // ordinary loads: nontemporal ones would fetch the line again for each
+    // of its eight 16-byte pieces (measured: 1.3x the bytes, twice the time)
     for (int64_t v0 = 0; v0 < seg / 16; v0 += 8) {     // one 128-byte line at a time
       uint4 line[8];
 #pragma unroll
-      for (int v = 0; v < 8; ++v) line[v] = load_stream(p + v0 + v);
+      for (int v = 0; v < 8; ++v) line[v] = p[v0 + v];
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const uint32_t w[4] = {line[v].x, line[v].y, line[v].z, line[v].w};

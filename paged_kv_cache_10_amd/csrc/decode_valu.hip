@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       const uint4* kr = reinterpret_cast<const uint4*>(kb);
       uint4 kv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kv[i] = load_stream(kr + k_piece(j, 8 * i + c));
+      for (int i = 0; i < 4; ++i) kv[i] = kr[k_piece(j, 8 * i + c)];
       float s[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int d = 64 * w + 8 * r + tg;
-      const uint4 vv = load_stream(reinterpret_cast<const uint4*>(vb) + v_piece(d, c));
+      const uint4 vv = reinterpret_cast<const uint4*>(vb)[v_piece(d, c)];
       float vf[8] = {bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y),
                      bf16_lo(vv.z), bf16_hi(vv.z), bf16_lo(vv.w), bf16_hi(vv.w)};
       if (ragged) {

@@ -1,4 +1,6 @@
-// probe_read: HBM read-bandwidth ceiling of this GPU, for three load patterns.
+// probe_read: HBM read-bandwidth ceiling of this GPU, for three load patterns
+// (the first two also with nontemporal loads, the kind the decode kernels
+// issue).
 //
 // Measures what a streaming reader can reach on the box, so the decode
 // kernel's bytes-per-second can be set against a measured ceiling as well as
@@ -9,7 +11,10 @@
 //            (LDS reserved to hold occupancy at the decode kernel's), each
 //            load instruction 1 KiB contiguous: the decode kernel's pattern;
 //   rows     the same blocks, but each instruction reads 16 rows of 512 B at
-//            64 B per row (MFMA operand rows over token-major data).
+//            64 B per row (MFMA operand rows over token-major data);
+//   stream_nt, blocks_nt  stream and blocks with every load marked
+//            nontemporal (the instruction's nt bit: lines streamed past the
+//            caches, not allocated in them).
 // Prints one JSON line.  Every load stays inside the buffer: indices are
 // bounded by construction and checked on the host before launch.
 #include <hip/hip_runtime.h>
@@ -32,19 +37,32 @@ constexpr size_t kU4 = kBytes / 16;            // uint4 elements
 constexpr int kBlockU4 = 2048;                 // 32 KiB
 constexpr int kBlocks = (int)(kU4 / kBlockU4); // 32,768
 
+template <bool kNT>
+__device__ __forceinline__ uint4 ld(const uint4* p) {
+  if constexpr (kNT) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
+template <bool kNT>
 __global__ void stream_kernel(const uint4* __restrict__ p, uint32_t* out) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   uint32_t acc = 0;
   for (; i + 3 * stride < kU4; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    const uint4 a = ld<kNT>(p + i), b = ld<kNT>(p + i + stride), c = ld<kNT>(p + i + 2 * stride),
+                d = ld<kNT>(p + i + 3 * stride);
     acc ^= a.x ^ b.y ^ c.z ^ d.w;
   }
   if (acc == 0x9e3779b9u) out[0] = acc;
 }
 
 // wave w of a work-group takes blocks w, w+4, ...; `rows` selects the pattern
-template <bool kRows>
+template <bool kRows, bool kNT>
 __global__ void block_kernel(const uint4* __restrict__ p, const int* __restrict__ order,
                              int per_wg, uint32_t* out) {
   extern __shared__ uint32_t reserve[];
@@ -66,7 +84,7 @@ __global__ void block_kernel(const uint4* __restrict__ p, const int* __restrict_
         for (int kb = 0; kb < 8; ++kb) v[16 + t * 8 + kb] = blk[1024 + (16 * t + r) * 32 + 4 * kb + q];
     } else {
 #pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = blk[j * 64 + lane];
+      for (int j = 0; j < 32; ++j) v[j] = ld<kNT>(blk + j * 64 + lane);
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc ^= v[j].x ^ v[j].w;
@@ -124,18 +142,29 @@ int main() {
     return ms / 20.0;
   };
   const double ms_stream = time_it([&] {
-    hipLaunchKernelGGL(stream_kernel, dim3(2 * cus), dim3(256), 0, 0, p, out);
+    hipLaunchKernelGGL(stream_kernel<false>, dim3(2 * cus), dim3(256), 0, 0, p, out);
   });
   const double ms_blocks = time_it([&] {
-    hipLaunchKernelGGL(block_kernel<false>, dim3(nwg), dim3(256), lds, 0, p, order, per_wg, out);
+    hipLaunchKernelGGL((block_kernel<false, false>), dim3(nwg), dim3(256), lds, 0, p, order, per_wg,
+                       out);
   });
   const double ms_rows = time_it([&] {
-    hipLaunchKernelGGL(block_kernel<true>, dim3(nwg), dim3(256), lds, 0, p, order, per_wg, out);
+    hipLaunchKernelGGL((block_kernel<true, false>), dim3(nwg), dim3(256), lds, 0, p, order, per_wg,
+                       out);
+  });
+  const double ms_stream_nt = time_it([&] {
+    hipLaunchKernelGGL(stream_kernel<true>, dim3(2 * cus), dim3(256), 0, 0, p, out);
+  });
+  const double ms_blocks_nt = time_it([&] {
+    hipLaunchKernelGGL((block_kernel<false, true>), dim3(nwg), dim3(256), lds, 0, p, order, per_wg,
+                       out);
   });
   printf("{\"device\": \"%s\", \"cus\": %d, \"bytes\": %zu, "
-         "\"stream_GBs\": %.1f, \"blocks_GBs\": %.1f, \"rows_GBs\": %.1f}\n",
+         "\"stream_GBs\": %.1f, \"blocks_GBs\": %.1f, \"rows_GBs\": %.1f, "
+         "\"stream_nt_GBs\": %.1f, \"blocks_nt_GBs\": %.1f}\n",
          prop.gcnArchName, cus, kBytes, kBytes / (ms_stream * 1e-3) / 1e9,
-         bytes_blocks / (ms_blocks * 1e-3) / 1e9, bytes_blocks / (ms_rows * 1e-3) / 1e9);
+         bytes_blocks / (ms_blocks * 1e-3) / 1e9, bytes_blocks / (ms_rows * 1e-3) / 1e9,
+         kBytes / (ms_stream_nt * 1e-3) / 1e9, bytes_blocks / (ms_blocks_nt * 1e-3) / 1e9);
   CHECK(hipFree(order));
   CHECK(hipFree(out));
   CHECK(hipFree(p));
