@@ -10,12 +10,14 @@
 //   * the tile finalize inside pkv_decode_attention, which merges the fixed
 //     groups of split partials that make up one tile (merge_kernel);
 //   * both at once for pkv_decode_attention_merged (merge2_kernel).
-// Two waves own one (row, output slot), 128 channels each (two per lane, so
-// more of the GPU's load queues work on a row and every load is 512
-// contiguous bytes), and each walks its input slots in increasing order with
-// one accumulator per channel, so the result is independent of scheduling,
-// an empty slot (lse = -inf) contributes exactly nothing and a lone slot
-// merges to itself bit for bit.
+// In merge_kernel two waves own one (row, output slot), 128 channels each
+// (two per lane, every load 512 contiguous bytes); merge_final_kernel and
+// merge2_kernel give each lane one channel, so four work-groups share a row
+// and its loads reach more compute units.  Every channel walks its input
+// slots in increasing order with one accumulator, so the result is
+// independent of scheduling and of how channels are spread over lanes, an
+// empty slot (lse = -inf) contributes exactly nothing and a lone slot merges
+// to itself bit for bit.
 #include "device.h"
 #include "kernels.h"
 
@@ -137,50 +139,54 @@ __global__ __launch_bounds__(kMergeThreads) void merge_final_kernel(MergeArgs a)
   if (part == 0 && lane == 0) a.out_lse[orow] = m + logf(wsum);
 }
 
+struct Merged1 {
+  float o;     // this lane's channel
+  float lse;
+};
+
 // The merge of the cnt slots lo .. lo+cnt-1 of a window of at most 64 slots
 // whose log-sum-exps sit in the lanes (lv at lane u = slot u) and whose
-// outputs are in LDS (win[u][lane]): merge_slots' arithmetic (the same max,
-// the same exp per slot, the slots summed in increasing order), so a group
-// merged here has the bits merge_slots gives it.  The outputs are read
-// eight slots at a time, so the LDS reads of a batch are in flight together.
-__device__ __forceinline__ Merged merge_window(float lv, int lo, int cnt, int lane,
-                                               const float2 (*win)[kMergeThreads]) {
+// outputs are in LDS (win[u][lane], one channel per lane): merge_slots'
+// arithmetic (the same max, the same exp per slot, the slots summed in
+// increasing order), so a group merged here has the bits merge_slots gives
+// it.  The outputs are read eight slots at a time, so the LDS reads of a
+// batch are in flight together.
+__device__ __forceinline__ Merged1 merge_window(float lv, int lo, int cnt, int lane,
+                                                const float (*win)[kMergeThreads]) {
   constexpr int kBatch = 8;
   const int hi = lo + cnt;
   const bool mine = lane >= lo && lane < hi;
   const float m = wave_max_nan(mine ? lv : -INFINITY);
-  if (m == -INFINITY) return Merged{make_float2(0.f, 0.f), -INFINITY};   // every slot empty
+  if (m == -INFINITY) return Merged1{0.f, -INFINITY};   // every slot empty
   const float wl = mine ? expf(lv - m) : 0.f;
-  float2 acc = make_float2(0.f, 0.f);
-  float wsum = 0.f;
+  float acc = 0.f, wsum = 0.f;
   for (int u0 = lo; u0 < hi; u0 += kBatch) {
-    float2 ou[kBatch];
+    float ou[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      ou[i] = (u0 + i < hi) ? win[u0 + i][lane] : make_float2(0.f, 0.f);
+    for (int i = 0; i < kBatch; ++i) ou[i] = (u0 + i < hi) ? win[u0 + i][lane] : 0.f;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (u0 + i < hi) {
         const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u0 + i));
         if (w != 0.f) {                        // uniform: 0 for an empty slot
-          acc.x = fmaf(w, ou[i].x, acc.x);
-          acc.y = fmaf(w, ou[i].y, acc.y);
+          acc = fmaf(w, ou[i], acc);
           wsum += w;
         }
       }
     }
   }
-  return Merged{make_float2(acc.x / wsum, acc.y / wsum), m + logf(wsum)};
+  return Merged1{acc / wsum, m + logf(wsum)};
 }
 
 // Tile finalize and final merge in one launch, for rows of at most 64 split
-// partials.  Four waves share one (row, 128-channel half): together they
-// load all of the row's split partials into LDS (slot u by wave u % 4, so
-// every load is in flight at once), wave w then merges groups j = w, w + 4,
-// ... into output slot j (as merge_kernel would), and wave 0 merges the
-// group results, kept in LDS, into fin_o / fin_lse (as merge_kernel over
-// those slots would), so the bits equal the two launches'.
+// partials.  Four waves share one (row, 64-channel quarter): together they
+// load the row's split partials into LDS (slot u by wave u % 4, so every
+// load is in flight at once), wave w then merges groups j = w, w + 4, ...
+// into output slot j (as merge_kernel would), and wave 0 merges the group
+// results, kept in LDS, into fin_o / fin_lse (as the final merge over those
+// slots would), so the bits equal the two launches'.
 constexpr int kMerge2Waves = 4;
+constexpr int kMerge2Parts = kHeadDim / kMergeThreads;   // one channel per lane
 
 __global__ __launch_bounds__(kMergeThreads * kMerge2Waves) void merge2_kernel(MergeArgs a,
                                                                                float* fin_o,
@@ -188,19 +194,18 @@ __global__ __launch_bounds__(kMergeThreads * kMerge2Waves) void merge2_kernel(Me
   constexpr int kPerWave = kMergeChunk / kMerge2Waves;
   const int row = blockIdx.x, part = blockIdx.z;
   const int w = threadIdx.x / kMergeThreads, lane = threadIdx.x % kMergeThreads;
-  __shared__ float2 split_o[kMergeChunk][kMergeThreads];
-  __shared__ float2 tile_o[kMergeChunk][kMergeThreads];
+  const int c = kMergeThreads * part + lane;      // this lane's channel
+  __shared__ float split_o[kMergeChunk][kMergeThreads];
+  __shared__ float tile_o[kMergeChunk][kMergeThreads];
   __shared__ float tile_lse[kMergeChunk];
   const float* lse_in = a.in_lse + (int64_t)row * a.in_slots;
-  const float2* o_in = reinterpret_cast<const float2*>(
-      a.in_o + (int64_t)row * a.in_slots * kHeadDim + 128 * part) + lane;
+  const float* o_in = a.in_o + (int64_t)row * a.in_slots * kHeadDim + c;
   {
-    float2 o[kPerWave];
+    float o[kPerWave];
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int u = kMerge2Waves * i + w;
-      o[i] = (u < a.in_slots) ? load_stream(o_in + (int64_t)u * (kHeadDim / 2))
-                              : make_float2(0.f, 0.f);
+      o[i] = (u < a.in_slots) ? __builtin_nontemporal_load(o_in + (int64_t)u * kHeadDim) : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
@@ -212,9 +217,9 @@ __global__ __launch_bounds__(kMergeThreads * kMerge2Waves) void merge2_kernel(Me
   __syncthreads();
   for (int j = w; j < a.n_out; j += kMerge2Waves) {
     const int lo = j * a.group;
-    const Merged r = merge_window(lv, lo, min(a.group, a.in_slots - lo), lane, split_o);
+    const Merged1 r = merge_window(lv, lo, min(a.group, a.in_slots - lo), lane, split_o);
     const int64_t orow = (int64_t)row * a.out_slots + a.out_slot0 + j;
-    reinterpret_cast<float2*>(a.out_o + orow * kHeadDim + 128 * part)[lane] = r.o;
+    a.out_o[orow * kHeadDim + c] = r.o;
     if (part == 0 && lane == 0) a.out_lse[orow] = r.lse;
     tile_o[j][lane] = r.o;
     if (lane == 0) tile_lse[j] = r.lse;
@@ -222,8 +227,8 @@ __global__ __launch_bounds__(kMergeThreads * kMerge2Waves) void merge2_kernel(Me
   __syncthreads();
   if (w != 0) return;
   const float tl = (lane < a.n_out) ? tile_lse[lane] : -INFINITY;   // lane j: group j's
-  const Merged r = merge_window(tl, 0, a.n_out, lane, tile_o);
-  reinterpret_cast<float2*>(fin_o + (int64_t)row * kHeadDim + 128 * part)[lane] = r.o;
+  const Merged1 r = merge_window(tl, 0, a.n_out, lane, tile_o);
+  fin_o[(int64_t)row * kHeadDim + c] = r.o;
   if (part == 0 && lane == 0) fin_lse[row] = r.lse;
 }
 
@@ -245,7 +250,7 @@ hipError_t launch_merge2(const MergeArgs& a, int rows, float* fin_o, float* fin_
                          hipStream_t stream) {
   if (rows <= 0 || a.n_out <= 0) return hipSuccess;
   if (a.in_slots > kMergeChunk) return hipErrorInvalidValue;   // one window per row
-  dim3 grid(rows, 1, kMergeParts);
+  dim3 grid(rows, 1, kMerge2Parts);
   hipLaunchKernelGGL(merge2_kernel, grid, dim3(kMergeThreads * kMerge2Waves), 0, stream, a,
                      fin_o, fin_lse);
   return hipGetLastError();
