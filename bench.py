@@ -46,6 +46,17 @@ PMC_TRAFFIC = {
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/decode_exact.h",
                   "paged_kv_cache_10_amd/csrc/device.h")
 
+# The same for the 4-request workload's decode call (LAUNCH["conc"]): the
+# decode kernel plus the tile finalize launch, FETCH_SIZE and WRITE_SIZE of
+# both dispatches added, calibrated on the plain copy of the same runs.
+PMC_TRAFFIC_CONC = {
+    "source_sha256": "e4580679264e04eaff4e7fafff1cd116257bc9c437ef3e6a3886c9d3eac8c947",
+    "workload": "conc", "tile": 8192, "split": 2048,
+    "fetch_kib": 254290.5 + 845.0, "fetch_scale": 1048576 / 524300.3,
+    "write_kib": 1584.3 + 387.0, "write_scale": 1.0,
+}
+CONC_SOURCES = KERNEL_SOURCES + ("paged_kv_cache_10_amd/csrc/merge.hip",)
+
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
@@ -82,12 +93,13 @@ def sources_sha256(files):
 def pmc_traffic(workload, tile, split, kernel):
     """Counter-derived HBM bytes per launch, or None if they were not taken
     on this kernel source and launch configuration."""
-    t = PMC_TRAFFIC
-    if (workload, tile, split, kernel) != (t["workload"], t["tile"], t["split"], "mfma"):
-        return None
-    if sources_sha256(KERNEL_SOURCES) != t["source_sha256"]:
-        return None
-    return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+    for t, sources in ((PMC_TRAFFIC, KERNEL_SOURCES), (PMC_TRAFFIC_CONC, CONC_SOURCES)):
+        if (workload, tile, split, kernel) != (t["workload"], t["tile"], t["split"], "mfma"):
+            continue
+        if sources_sha256(sources) != t["source_sha256"]:
+            return None
+        return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+    return None
 
 
 # Launch configuration timed for each workload (tile tokens; tokens per
@@ -361,6 +373,7 @@ def main():
     tok_s = B / (ms_step * 1e-3)
     kv_bytes_layer = kv_bytes_step // L
     dec_gbs = kv_bytes_layer / (dec_avg_ms * 1e-3) / 1e9
+    lengths = w.max_ctx if len(set(w.ctx_lens)) == 1 else "mixed"
 
     res = {
         "metric": "decode attention KV GB/s (% of HBM peak) and tokens/s at 262K ctx, 1 GPU",
@@ -376,7 +389,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: {B} x {w.max_ctx if B == 1 else 'mixed'} tokens, {L} layers, "
+            "workload": f"{w.name}: {B} x {lengths} tokens, {L} layers, "
                         f"{Hq} q / {Hkv} kv heads, head_dim {D}, 64-token pages, "
                         + (f"per-request tiles planned for {plan} work-groups (at most "
                            f"{max_row} tokens, {max_tiles} per request)" if plan else f"tile {T}")
