@@ -25,8 +25,8 @@ namespace pkv {
 
 namespace {
 
-constexpr int kMergeThreads = 64;     // one wave; lane i owns channels 128 * half + 2i, +1
-constexpr int kMergeParts = kHeadDim / 128;   // waves per (row, output slot)
+constexpr int kMergeThreads = 64;     // one wave (merge_kernel: lane i owns channels 128 * half + 2i, +1)
+constexpr int kMergeParts = kHeadDim / 128;   // merge_kernel: waves per (row, output slot)
 constexpr int kMergeChunk = 64;       // input slots whose loads are in flight together
 
 struct Merged {
