@@ -200,9 +200,10 @@ def main():
     if (args.tile or args.split or args.staged or args.kernel != "mfma" or args.host_staged
             or args.compact_older):
         plan = 0
-    w.tile_tokens = args.tile or launch.get("tile", w.tile_tokens)
     # a 32,768-token window decoded alone holds 1/8 of the history: 512-token
-    # splits give its launch 256 work-groups (4,096-token ones only 32)
+    # splits give its launch 256 work-groups (4,096-token ones only 32), and
+    # 512-token tiles (64 partials per head per window) need no tile finalize
+    w.tile_tokens = args.tile or (512 if args.staged else launch.get("tile", w.tile_tokens))
     args.split = args.split or (512 if args.staged else launch.get("split", 0))
     overlap = args.overlap and not args.serial
     T = w.tile_tokens
@@ -414,7 +415,10 @@ def main():
             "bound": "hbm",
             "kernel": "decode_mfma_kernel" if args.kernel == "mfma" else "decode_valu_kernel",
             "launch": ("one pkv_decode_attention_rows call per layer = the decode kernel" if plan
-                       else "one pkv_decode_attention call per layer = the decode kernel"
+                       else (f"{span // window} pkv_decode_attention calls per layer (one per "
+                             f"{window}-token window), each" if window < span
+                             else "one pkv_decode_attention call per layer =")
+                       + " the decode kernel"
                        + ("" if ws_bytes == 0 else " + the tile finalize")),
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
