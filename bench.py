@@ -90,6 +90,56 @@ def sources_sha256(files):
     return h.hexdigest()
 
 
+def time_graph(L, K, stream, use_merged, decode_layer, pkv, pool, qs, dt, dc, span, T, w, po, pl,
+               outs, lses, ws, args, timed_o, timed_l, same):
+    """The timed step (every layer's decode and merge) captured once in a HIP
+    graph on a side stream and replayed: the replay time per step, and three
+    replays, each after the outputs are poisoned by eager work, checked bit
+    for bit against the eager step."""
+    import torch
+    gs = torch.cuda.Stream()               # default priority
+
+    def gstep():
+        for layer in range(L):
+            if use_merged:
+                pkv.decode_attention_merged(pool, layer, qs[layer], dt, dc, span, T, w.scale,
+                                            po[layer], pl[layer], outs[layer], lses[layer],
+                                            workspace=ws, kernel=args.kernel,
+                                            split_tokens=args.split, stream=gs)
+            else:
+                decode_layer(layer, gs)
+                pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=gs)
+
+    gs.wait_stream(stream)
+    gstep()                                 # eager, on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        gstep()
+    torch.cuda.synchronize()
+    ok = True
+    for _ in range(3):
+        outs.fill_(float("nan"))
+        lses.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = ok and same(outs, timed_o) and same(lses, timed_l)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    for _ in range(K):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    del g
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(ms, 4), "replays_equal_eager_bitwise": ok,
+            "kv_GBs": round(w.kv_bytes_per_step / (ms * 1e-3) / 1e9, 1)}
+
+
 def pmc_traffic(workload, tile, split, kernel):
     """Counter-derived HBM bytes per launch, or None if they were not taken
     on this kernel source and launch configuration."""
@@ -165,6 +215,8 @@ def parse():
     ap.add_argument("--merge-stress", action="store_true",
                     help="time pkv_merge_partials alone on 64 x 24 rows x 256 partials; "
                          "prints its own JSON line")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the timed step in a HIP graph and time its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
@@ -253,16 +305,17 @@ def main():
     decoded = [torch.cuda.Event() for _ in range(L)]
     merged = torch.cuda.Event()
 
-    def decode_layer(layer):
+    def decode_layer(layer, s=None):
+        s = stream if s is None else s
         if plan:
             pkv.decode_attention_rows(pool, layer, qs[layer], dt, dc, d_rt, max_row, max_tiles,
-                                      w.scale, po[layer], pl[layer], stream=stream)
+                                      w.scale, po[layer], pl[layer], stream=s)
             return
         for begin in range(0, span, window):
             pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc,
                                  begin, min(window, span - begin), T, w.scale, po[layer],
                                  pl[layer], workspace=ws, kernel=args.kernel,
-                                 split_tokens=args.split, stream=stream)
+                                 split_tokens=args.split, stream=s)
 
     # a whole-history fixed tiling decodes and merges each layer in one call
     # (one kernel boundary fewer where tiles hold several splits); the
@@ -348,6 +401,12 @@ def main():
         pkv.merge_partials(po[layer], pl[layer], outs[layer], lses[layer], stream=stream)
     torch.cuda.synchronize()
     self_check = same(ref_o, outs) and same(ref_l, lses)
+
+    # optionally: the timed step captured once in a HIP graph and replayed
+    graph_res = None
+    if args.graph:
+        graph_res = time_graph(L, K, stream, use_merged, decode_layer, pkv, pool, qs, dt, dc,
+                               span, T, w, po, pl, outs, lses, ws, args, timed_o, timed_l, same)
     timed_check = same(timed_o, outs) and same(timed_l, lses)
 
     if args.host_staged and args.compact_older:
@@ -430,6 +489,7 @@ def main():
         },
         "setup_s": round(t_gen, 1),
         "overlapped_equals_serial_bitwise": self_check,
+        **({"graph": graph_res} if graph_res is not None else {}),
         "timed_equals_serial_bitwise": timed_check,
         ("serial_merges" if overlap else "overlapped_merges"): {
             "ms_per_step": round(ms_other, 4),
