@@ -57,6 +57,15 @@ PMC_TRAFFIC_CONC = {
 }
 CONC_SOURCES = KERNEL_SOURCES + ("paged_kv_cache_10_amd/csrc/merge.hip",)
 
+# The same for the mixed batch's decode call with per-request tiles planned
+# for LAUNCH["mixed"]["plan"] work-groups (the decode kernel alone).
+PMC_TRAFFIC_MIXED = {
+    "source_sha256": PMC_TRAFFIC["source_sha256"],
+    "workload": "mixed", "plan": 256,
+    "fetch_kib": 854222.6, "fetch_scale": 1048576 / 524301.1,
+    "write_kib": 5922.3, "write_scale": 1.0,
+}
+
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
@@ -140,9 +149,15 @@ def time_graph(L, K, stream, use_merged, decode_layer, pkv, pool, qs, dt, dc, sp
             "kv_GBs": round(w.kv_bytes_per_step / (ms * 1e-3) / 1e9, 1)}
 
 
-def pmc_traffic(workload, tile, split, kernel):
+def pmc_traffic(workload, tile, split, kernel, plan=0):
     """Counter-derived HBM bytes per launch, or None if they were not taken
     on this kernel source and launch configuration."""
+    if plan:
+        t = PMC_TRAFFIC_MIXED
+        if ((workload, plan, kernel) != (t["workload"], t["plan"], "mfma")
+                or sources_sha256(KERNEL_SOURCES) != t["source_sha256"]):
+            return None
+        return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
     for t, sources in ((PMC_TRAFFIC, KERNEL_SOURCES), (PMC_TRAFFIC_CONC, CONC_SOURCES)):
         if (workload, tile, split, kernel) != (t["workload"], t["tile"], t["split"], "mfma"):
             continue
@@ -485,7 +500,7 @@ def main():
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_ms": round(dec_avg_ms, 5),
-            "traffic": None if plan else pmc_traffic(args.workload, T, args.split, args.kernel),
+            "traffic": pmc_traffic(args.workload, T, args.split, args.kernel, plan),
         },
         "setup_s": round(t_gen, 1),
         "overlapped_equals_serial_bitwise": self_check,
