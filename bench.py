@@ -50,10 +50,10 @@ KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_
 # decode kernel plus the tile finalize launch, FETCH_SIZE and WRITE_SIZE of
 # both dispatches added, calibrated on the plain copy of the same runs.
 PMC_TRAFFIC_CONC = {
-    "source_sha256": "e4580679264e04eaff4e7fafff1cd116257bc9c437ef3e6a3886c9d3eac8c947",
+    "source_sha256": "a4f14d4c7a2e39100d5b7e488bbad82c4ff6d887b461ca1939ba595d538164e5",
     "workload": "conc", "tile": 8192, "split": 2048,
-    "fetch_kib": 254290.5 + 845.0, "fetch_scale": 1048576 / 524300.3,
-    "write_kib": 1584.3 + 387.0, "write_scale": 1.0,
+    "fetch_kib": 254290.4 + 845.0, "fetch_scale": 1048576 / 524300.4,
+    "write_kib": 1584.4 + 387.0, "write_scale": 1.0,
 }
 CONC_SOURCES = KERNEL_SOURCES + ("paged_kv_cache_10_amd/csrc/merge.hip",)
 

@@ -1,0 +1,54 @@
+"""CPU: the host-side rules of bench.py that decide what its JSON line may
+claim (no GPU needed).
+
+  * counter-derived traffic is reported only for the kernel sources and
+    launch shapes the counters were taken on, and is within a few per mille
+    of the algorithmic bytes there;
+  * a request for more than one GPU is refused with a message, before
+    anything touches a device."""
+
+import os
+import subprocess
+import sys
+
+import bench
+from paged_kv_cache_10_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kv_bytes_per_layer(name):
+    w = I.workload(name)
+    return w.kv_bytes_per_step // w.num_layers
+
+
+def test_traffic_only_for_measured_shapes():
+    assert bench.pmc_traffic("long262k", 4096, 4096, "mfma") is not None
+    assert bench.pmc_traffic("long262k", 4096, 2048, "mfma") is None      # another split
+    assert bench.pmc_traffic("long262k", 4096, 4096, "valu") is None      # another kernel
+    assert bench.pmc_traffic("conc", 8192, 2048, "mfma") is not None
+    assert bench.pmc_traffic("conc", 8192, 1024, "mfma") is None
+    assert bench.pmc_traffic("mixed", 4096, 4096, "mfma", plan=256) is not None
+    assert bench.pmc_traffic("mixed", 4096, 4096, "mfma", plan=512) is None
+    assert bench.pmc_traffic("mixed", 4096, 4096, "mfma") is None          # fixed tiling
+
+
+def test_traffic_close_to_algorithmic_bytes():
+    for name, tile, split, plan in (("long262k", 4096, 4096, 0), ("conc", 8192, 2048, 0),
+                                    ("mixed", 4096, 4096, 256)):
+        ratio = bench.pmc_traffic(name, tile, split, "mfma", plan) / kv_bytes_per_layer(name)
+        assert 1.0 <= ratio < 1.01, (name, ratio)
+
+
+def test_traffic_dropped_when_the_kernel_source_changes(monkeypatch):
+    monkeypatch.setattr(bench, "sources_sha256", lambda files: "0" * 64)
+    assert bench.pmc_traffic("long262k", 4096, 4096, "mfma") is None
+    assert bench.pmc_traffic("conc", 8192, 2048, "mfma") is None
+    assert bench.pmc_traffic("mixed", 4096, 4096, "mfma", plan=256) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert p.returncode != 0
+    assert "one GPU" in (p.stdout + p.stderr)
