@@ -245,7 +245,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
               "(no multi-GPU path exists)", file=sys.stderr)
         return 2
     ceiling = None if args.no_read_probe else read_probe()
