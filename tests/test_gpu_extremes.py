@@ -8,6 +8,9 @@
     reach a few hundred and the running max jumps by hundreds between
     pages; against the float64 oracle at the usual tolerances.
   * a single key (ctx = 1): out = that key's V row, lse = its score.
+  * q = 0 over runs of two representations (older pages compact, the rest
+    exact, one launch): out = the mean of the values the two runs hold
+    (compact codes times their scale, exact bf16), lse = ln(ctx).
 
 Tolerances: max abs error 2e-3 on outputs and 1e-4 on log-sum-exp."""
 
@@ -18,7 +21,8 @@ import pytest
 import torch
 
 from paged_kv_cache_10_amd import inputs as I
-from gpu_helpers import (Case, assert_lse_close, assert_out_close, check_layer)
+from oracle import compact as C
+from gpu_helpers import (Case, Runs, assert_lse_close, assert_out_close, check_layer, kv_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +89,26 @@ def test_single_key_is_its_value(case):
     exp_lse = np.einsum("hd,hd->h", q, k[heads, 0]) * w.scale
     assert_out_close(o[b], v[heads, 0], what="out")
     assert_lse_close(l[b], exp_lse, what="lse")
+
+
+def test_zero_query_over_compact_and_exact_runs(case):
+    w = case.w
+    grp = w.num_q_heads // w.num_kv_heads
+    compact = [(c // 2) // 64 * 64 for c in w.ctx_lens]        # whole pages, about half
+    runs = Runs(case, compact, seed=7)
+    tile, etile = 1024, 512
+
+    def run():
+        case.q[0].zero_()
+        return runs.decode(0, tile, etile=etile, one_launch=True)
+
+    _, _, o, l = [t.cpu().numpy() for t in _with_q(case, run)]
+    for b, ctx in enumerate(w.ctx_lens):
+        if ctx == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+            continue
+        _, vb = kv_bits(case, 0, b)
+        v2 = np.stack([C.two_runs(vb[g], compact[b]) for g in range(w.num_kv_heads)])
+        exp_o = np.repeat(v2[:, :ctx].mean(axis=1), grp, axis=0)
+        assert_out_close(o[b], exp_o, what=f"out b={b}")
+        assert_lse_close(l[b], np.full(w.num_q_heads, math.log(ctx)), what=f"lse b={b}")
