@@ -395,11 +395,13 @@ int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
  * each of max_batch x window_tokens/64 pages, and three caller streams:
  *   copy       host -> device window copies;
  *   compute    the caller's work on a lease (decode, append) runs here;
- *   writeback  device -> host copies of changed tail pages.
+ *   writeback  device -> host write-back of changed tail rows.
  * Ordering is on the device: a window's copy waits for the previous readers
- * of the buffer it overwrites (that lease's consumer and write-back events),
- * the compute stream waits for the copy, and the write-back waits for the
- * compute stream's consumer event.  Only pkv_stager_retire blocks the host.
+ * of the buffer it overwrites (that lease's consumer and write-back events)
+ * and, when it reads a host page that received a tail row since the last
+ * retire, for the latest write-back; the compute stream waits for the copy,
+ * and the write-back waits for the compute stream's consumer event.  Only
+ * pkv_stager_retire blocks the host.
  * Each window's copy is split in two: the first half on `copy`, the second
  * on a stream the stager creates and owns (default priority, destroyed with
  * the stager), so one copy's wait overlaps the other's transfer.
@@ -410,10 +412,15 @@ int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
  * table (entry i of row b = logical page window_begin/64 + i) to pass to
  * pkv_decode_attention / pkv_append_kv with the staging pool and
  * lease.staging_layer, on the compute stream.  pkv_lease_seal records the
- * consumer event after that work and, if write_back_tail, copies back the
- * pages holding each request's last token (ctx_lens[b] - 1) when they lie in
- * the window.  A new lease may begin only after the previous one is sealed;
- * a seal must name the open lease.  Stage generations only increase.
+ * consumer event after that work and, if write_back_tail, writes back the
+ * changed tail rows only: the K and V of each request's last token
+ * (ctx_lens[b] - 1) when it lies in the window, 2 x num_kv_heads x 256 bf16
+ * per request (4,096 bytes at 4 KV heads), stored into the host page by a
+ * kernel on the write-back stream (GPU memory management page, "Staging as
+ * a lease").  For a bf16 staging pool the host arena must be pinned memory
+ * the device can address (hipHostMalloc); create fails otherwise.  A new
+ * lease may begin only after the previous one is sealed; a seal must name
+ * the open lease.  Stage generations only increase.
  * pkv_stager_retire waits for every sealed lease and returns their count as
  * receipts.  Any HIP failure quarantines the stager: begin and seal are
  * refused, retire drains the copy, write-back and compute streams and the

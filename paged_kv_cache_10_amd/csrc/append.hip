@@ -37,7 +37,39 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   vb[v_piece(tid, j >> 3) * 8 + (j & 7)] = vrow[tid];
 }
 
+// One work-group of 256 threads per (KV head, row): threads 0..31 copy the
+// token's 32 K pieces (16 bytes each, a piece holds 8 channels of one
+// token), every thread its channel's V element (2 bytes inside the channel's
+// 8-token piece).  The stores then reach system scope before the kernel
+// ends, so a copy ordered after this launch reads them from host memory.
+__global__ __launch_bounds__(256) void writeback_kernel(WritebackArgs a) {
+  const int g = blockIdx.x;
+  const TailRow r = a.rows[blockIdx.y];
+  const int tid = threadIdx.x;
+  if (r.src_page < 0 || r.src_page >= a.src_num_pages || r.dst_page < 0 ||
+      r.dst_page >= a.dst_num_pages || r.token < 0 || r.token >= kPageTokens)
+    return;                                                // not a row of either arena
+  const int j = r.token;
+  const int64_t kofs = (int64_t)g * kPageTokens * kHeadDim;
+  const int64_t vofs = (int64_t)(a.num_kv_heads + g) * kPageTokens * kHeadDim;
+  const uint16_t* sp = a.src + a.src_layer_off + (int64_t)r.src_page * a.page_elems;
+  uint16_t* dp = a.dst + a.dst_layer_off + (int64_t)r.dst_page * a.page_elems;
+  if (tid < kHeadDim / 8) {
+    const int i = k_piece(j, tid);
+    reinterpret_cast<uint4*>(dp + kofs)[i] = reinterpret_cast<const uint4*>(sp + kofs)[i];
+  }
+  const int e = v_piece(tid, j >> 3) * 8 + (j & 7);
+  dp[vofs + e] = sp[vofs + e];
+  __threadfence_system();
+}
+
 }  // namespace
+
+hipError_t launch_writeback(const WritebackArgs& a, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(writeback_kernel, dim3(a.num_kv_heads, a.n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;

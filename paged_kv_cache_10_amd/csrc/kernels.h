@@ -51,6 +51,32 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
 
+// Tail write-back: for each listed row, the K and V elements of one token
+// copied from a page of one arena to the same token of a page of another
+// (a host arena in pinned memory the device addresses), in the block layout,
+// byte for byte: 2 x num_kv_heads x 256 bf16 per row, nothing else.
+struct TailRow {
+  int32_t src_page;          // page of the source arena (0..src_num_pages-1)
+  int32_t dst_page;          // page of the destination arena (0..dst_num_pages-1)
+  int32_t token;             // token within the page (0..63)
+  int32_t unused;
+};
+constexpr int kMaxTailRows = 128;   // rows per launch (kernel-argument space)
+struct WritebackArgs {
+  const uint16_t* src;       // source arena
+  int64_t src_layer_off;     // element offset of the source layer's slab
+  int64_t src_num_pages;
+  uint16_t* dst;             // destination arena (device address)
+  int64_t dst_layer_off;
+  int64_t dst_num_pages;
+  int64_t page_elems;        // bf16 elements of one (layer, page), both arenas
+  int32_t num_kv_heads;
+  int32_t n;                 // rows used (1..kMaxTailRows)
+  TailRow rows[kMaxTailRows];
+};
+
+hipError_t launch_writeback(const WritebackArgs& a, hipStream_t stream);
+
 // Largest query group each kernel supports.
 constexpr int kValuMaxGroup = 8;
 constexpr int kMfmaMaxGroup = 16;

@@ -5,8 +5,11 @@
 // layers under a lease"; GPU memory management, "Staging as a lease").
 //
 // Ordering is on the device: the copy streams wait for the previous readers
-// of the buffer they overwrite, the compute stream waits for the copies, the
-// write-back stream waits for the compute stream's consumer event.  Each
+// of the buffer they overwrite and for any write-back still landing in a
+// host page they read, the compute stream waits for the copies, the
+// write-back stream waits for the compute stream's consumer event.  Only the
+// changed tail rows are written back (one token per request), by a kernel
+// that stores them into the pinned host pages.  Each
 // window's copy is split in two halves, one on the caller's copy stream and
 // one on a second copy stream the stager owns (default priority), so that one
 // copy engine's wait before a window overlaps the other's transfer.  The host
@@ -18,6 +21,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <new>
+#include <unordered_set>
 #include <vector>
 
 #include "kernels.h"
@@ -38,9 +42,10 @@ struct Buffer {
   bool wrote_back = false;
 };
 
-struct Tail {                      // a changed tail page to copy back at seal
+struct Tail {                      // a changed tail row to copy back at seal
   int64_t staging_page;
   int64_t host_page;
+  int32_t token;                   // token within the page
 };
 
 }  // namespace
@@ -48,6 +53,7 @@ struct Tail {                      // a changed tail page to copy back at seal
 struct pkv_stager {
   const pkv_pool* staging;
   char* host;                      // pinned host arena, layout of a pool of host_pages pages
+  char* host_dev = nullptr;        // the same memory as the device addresses it
   int64_t host_pages;
   int32_t host_layers;
   int32_t max_batch;
@@ -69,6 +75,11 @@ struct pkv_stager {
   std::vector<Tail> open_tails;
   int64_t sealed_unretired = 0;    // leases sealed since the last retire
   bool quarantined = false;
+  // Host pages (layer * host_pages + page) written back since the last
+  // retire, and an event after the latest write-back: the write-back stream
+  // runs in order, so a copy that waits for it reads every earlier row too.
+  std::unordered_set<int64_t> wb_pending;
+  hipEvent_t wb_last = nullptr;
 };
 
 namespace {
@@ -137,6 +148,13 @@ PKV_API int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_
   for (int64_t i = 0; i < need; ++i) t[(size_t)i] = (int32_t)i;
   hipError_t e = hipMemcpy(dev_tables, t.data(), sizeof(int32_t) * (size_t)need, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&st->copy2, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&st->wb_last, hipEventDisableTiming);
+  if (e == hipSuccess && !compact) {
+    // the tail write-back kernel stores into the host pages directly
+    void* dev = nullptr;
+    e = hipHostGetDevicePointer(&dev, host_arena, 0);
+    st->host_dev = static_cast<char*>(dev);
+  }
   for (auto& bf : st->buffers) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bf.copied, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&bf.copied2, hipEventDisableTiming);
@@ -151,8 +169,12 @@ PKV_API int pkv_stager_create(const pkv_pool* staging, void* host_arena, uint64_
       if (bf.written) (void)hipEventDestroy(bf.written);
     }
     if (st->copy2) (void)hipStreamDestroy(st->copy2);
+    if (st->wb_last) (void)hipEventDestroy(st->wb_last);
     delete st;
-    return pkv::set_error(PKV_ERR_DEVICE, "stager setup failed: %s", hipGetErrorString(e));
+    return pkv::set_error(PKV_ERR_DEVICE,
+                          "stager setup failed: %s (host_arena must be pinned host memory, "
+                          "e.g. hipHostMalloc, which the device can address)",
+                          hipGetErrorString(e));
   }
   *out = st;
   pkv::clear_error();
@@ -189,17 +211,27 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
                               "(0..%lld)", b, (long long)lp, hp, (long long)(st->host_pages - 1));
     }
   }
+  // a host page this window reads may still be receiving an earlier lease's
+  // tail row: then the copies also wait for the latest write-back
+  bool reads_pending = false;
+  if (!st->wb_pending.empty()) {
+    const int64_t lbase = (int64_t)layer * st->host_pages;
+    for (int b = 0; b < batch && !reads_pending; ++b) {
+      const int64_t end = std::min<int64_t>(host_ctx_lens[b], (int64_t)window_begin + st->window_tokens);
+      for (int64_t lp = first; lp * PT < end && !reads_pending; ++lp)
+        reads_pending = st->wb_pending.count(lbase + host_table[(int64_t)b * pt_stride + lp]) > 0;
+    }
+  }
   const int32_t k = (int32_t)(st->generation % (uint64_t)st->num_buffers);
   Buffer& bf = st->buffers[k];
   hipError_t e = hipSuccess;
   // the previous readers of buffer k must finish before the copies overwrite it
-  if (bf.has_readers) {
-    for (hipStream_t cs : {st->copy, st->copy2}) {
-      if (e == hipSuccess) e = hipStreamWaitEvent(cs, bf.consumed, 0);
-      if (e == hipSuccess && bf.wrote_back) e = hipStreamWaitEvent(cs, bf.written, 0);
-    }
-    if (e != hipSuccess) return quarantine(st, e, "wait for the buffer's readers");
+  for (hipStream_t cs : {st->copy, st->copy2}) {
+    if (e == hipSuccess && bf.has_readers) e = hipStreamWaitEvent(cs, bf.consumed, 0);
+    if (e == hipSuccess && bf.has_readers && bf.wrote_back) e = hipStreamWaitEvent(cs, bf.written, 0);
+    if (e == hipSuccess && reads_pending) e = hipStreamWaitEvent(cs, st->wb_last, 0);
   }
+  if (e != hipSuccess) return quarantine(st, e, "wait for the buffer's readers");
   const uint64_t plb = st->staging->page_layer_bytes;
   char* slab = static_cast<char*>(st->staging->base);        // staging layer 0
   const char* hslab = st->host + (uint64_t)layer * (uint64_t)st->host_pages * plb;
@@ -232,7 +264,8 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
     }
     if (ctx > window_begin && ctx <= (int64_t)window_begin + st->window_tokens) {
       const int64_t lp = (ctx - 1) / PT;                     // the request's tail page is here
-      tails.push_back({dst0 + (lp - first), host_table[(int64_t)b * pt_stride + lp]});
+      tails.push_back({dst0 + (lp - first), host_table[(int64_t)b * pt_stride + lp],
+                       (int32_t)((ctx - 1) % PT)});
     }
   }
   if (e == hipSuccess) e = hipEventRecord(bf.copied, st->copy);
@@ -267,16 +300,32 @@ PKV_API int pkv_lease_seal(pkv_stager* st, const pkv_lease* lease, int32_t write
   hipError_t e = hipEventRecord(bf.consumed, st->compute);
   bool wrote = false;
   if (e == hipSuccess && write_back_tail && !st->open_tails.empty()) {
+    // the changed rows only: one token of K and V per request whose tail is
+    // in the window, 2 x Hkv x 256 bf16 each, stored into the host page
     e = hipStreamWaitEvent(st->writeback, bf.consumed, 0);
-    const uint64_t plb = st->staging->page_layer_bytes;
-    const char* slab = static_cast<const char*>(st->staging->base);
-    char* hslab = st->host + (uint64_t)lease->layer * (uint64_t)st->host_pages * plb;
-    for (const Tail& t : st->open_tails) {
-      if (e != hipSuccess) break;
-      e = hipMemcpyAsync(hslab + (uint64_t)t.host_page * plb, slab + (uint64_t)t.staging_page * plb,
-                         (size_t)plb, hipMemcpyDeviceToHost, st->writeback);
+    const int64_t page_elems = (int64_t)(st->staging->page_layer_bytes / 2);
+    pkv::WritebackArgs w;
+    w.src = static_cast<const uint16_t*>(st->staging->base);
+    w.src_layer_off = 0;
+    w.src_num_pages = st->staging->num_pages;
+    w.dst = reinterpret_cast<uint16_t*>(st->host_dev);
+    w.dst_layer_off = page_elems * st->host_pages * lease->layer;
+    w.dst_num_pages = st->host_pages;
+    w.page_elems = page_elems;
+    w.num_kv_heads = st->staging->geom.num_kv_heads;
+    const int64_t lbase = (int64_t)lease->layer * st->host_pages;
+    size_t i = 0;
+    while (e == hipSuccess && i < st->open_tails.size()) {
+      w.n = 0;
+      for (; i < st->open_tails.size() && w.n < pkv::kMaxTailRows; ++i, ++w.n) {
+        const Tail& t = st->open_tails[i];
+        w.rows[w.n] = {(int32_t)t.staging_page, (int32_t)t.host_page, t.token, 0};
+        st->wb_pending.insert(lbase + t.host_page);
+      }
+      e = pkv::launch_writeback(w, st->writeback);
     }
     if (e == hipSuccess) e = hipEventRecord(bf.written, st->writeback);
+    if (e == hipSuccess) e = hipEventRecord(st->wb_last, st->writeback);
     wrote = true;
   }
   if (e != hipSuccess) return quarantine(st, e, "seal");
@@ -319,6 +368,7 @@ PKV_API int pkv_stager_retire(pkv_stager* st, int64_t* receipts) {
   }
   if (receipts) *receipts = st->sealed_unretired;
   st->sealed_unretired = 0;
+  st->wb_pending.clear();            // every write-back has landed
   st->quarantined = false;
   for (auto& bf : st->buffers) bf.has_readers = bf.wrote_back = false;
   pkv::clear_error();
@@ -356,6 +406,7 @@ PKV_API int pkv_stager_destroy(pkv_stager* st) {
     (void)hipEventDestroy(bf.written);
   }
   (void)hipStreamDestroy(st->copy2);
+  (void)hipEventDestroy(st->wb_last);
   delete st;
   pkv::clear_error();
   return PKV_OK;

@@ -95,8 +95,8 @@ def test_staged_from_host_equals_resident(gpu, num_buffers):
 
 def test_appended_tail_flows_back_to_host(gpu):
     """The new token is appended in the staging buffer, attended, and its
-    page is written back: the host copy then equals one built directly with
-    the longer history, and the decode matches the oracle."""
+    K and V rows are written back: the host copy then equals one built
+    directly with the longer history, and the decode matches the oracle."""
     w = workload()
     longer = I.Workload("staged", seed=51, ctx_lens=[c + 1 for c in w.ctx_lens], num_layers=2,
                         tile_tokens=4096)
@@ -124,6 +124,55 @@ def test_appended_tail_flows_back_to_host(gpu):
                         before_decode=append, write_back=True)
         check_layer(ref_case, layer, got, ref_case.oracle_layer(layer))
     assert st.stager.retire() == 6
+    np.testing.assert_array_equal(st.host.numpy().view(np.uint16), host_long)
+    st.stager.destroy()
+
+
+def test_second_step_waits_for_the_first_write_back(gpu):
+    """Two steps of append + decode + tail write-back on one layer, with two
+    staging buffers and no retire in between.  The second lease uses a
+    buffer with no earlier readers, so only the wait on the pending
+    write-back keeps its copy from reading the tail page before the first
+    step's row has landed in the host copy.  Each step's decode matches the
+    oracle and the resident decode of the same history bit for bit, and the
+    host copy ends as the history of ctx + 2 tokens (only the two appended
+    rows were written, not the ghost token beside them)."""
+    base = I.Workload("staged", seed=53, ctx_lens=[100, 20000, 31000], num_layers=1,
+                      tile_tokens=4096)
+    steps = [I.Workload("staged", seed=53, ctx_lens=[c + s for c in base.ctx_lens], num_layers=1,
+                        tile_tokens=4096) for s in (1, 2)]
+    assert [w.pages_per_req for w in steps] == [base.pages_per_req] * 2
+    table = I.draw_page_tables(steps[1], WINDOW // 64)
+    host_short, _ = I.host_pool(base, table, fill=0, pad_value=0)
+    host_long, _ = I.host_pool(steps[1], table, fill=0, pad_value=0)
+    st = Staging(base, table, host_short, num_buffers=2)
+    last = steps[1]
+    for w in steps:
+        k_new = torch.empty((w.batch, 4, 256), dtype=torch.bfloat16, device=DEV)
+        v_new = torch.empty_like(k_new)
+        for b, c in enumerate(w.ctx_lens):
+            kb, vb = I.draw_kv(last, 0, b)
+            k_new[b] = torch.from_numpy(kb[:, c - 1].view(np.int16)).view(torch.bfloat16)
+            v_new[b] = torch.from_numpy(vb[:, c - 1].view(np.int16)).view(torch.bfloat16)
+        pos = torch.tensor([c - 1 for c in w.ctx_lens], dtype=torch.int32, device=DEV)
+        # a ghost token one past the new length, in the same staging page:
+        # never attended, and a write-back of changed rows only leaves the
+        # host copy without it
+        ghost_pos = torch.tensor(w.ctx_lens, dtype=torch.int32, device=DEV)
+        ghost = torch.full_like(k_new, 1.0)
+
+        def append(lease, tab, begin):
+            pkv.append_kv(st.pool, lease.staging_layer, tab, pos, k_new, v_new, stream=st.compute)
+            pkv.append_kv(st.pool, lease.staging_layer, tab, ghost_pos, ghost, ghost,
+                          stream=st.compute)
+
+        ref_case = Case(w, table=table)
+        got = st.decode(0, ref_case.q[0], 4096, 4096, ctx=w.ctx_lens, before_decode=append,
+                        write_back=True)
+        check_layer(ref_case, 0, got, ref_case.oracle_layer(0))
+        for x, y in zip(ref_case.decode(0, tile=4096, split=4096), got):
+            assert same_bits(x, y)
+    assert st.stager.retire() == 2
     np.testing.assert_array_equal(st.host.numpy().view(np.uint16), host_long)
     st.stager.destroy()
 
