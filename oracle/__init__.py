@@ -25,11 +25,15 @@ other than itself: brute force with exact summation, library routines
 (torch's scaled-dot-product attention, scipy's logsumexp), closed forms,
 hand-derived golden fixtures and planted mistakes; ``compact`` by
 ``tests/test_oracle_compact.py``.
+
+``admission`` is a plain planner of which logical pages of which contexts
+hold device pages each step (Staging without a stall, section "Admission
+that does arithmetic"; GPU memory management, section "Pages held by right,
+borrowed or free"), pinned by ``tests/test_oracle_admission.py``.
 """
 
 from .attention import (  # noqa: F401
     widen_bf16,
-    kv_head_of,
     attend,
     tile_bounds,
     tile_partials,
@@ -39,4 +43,4 @@ from .attention import (  # noqa: F401
     stress_partials,
     union_attention,
 )
-from . import compact  # noqa: F401
+from . import admission, compact  # noqa: F401

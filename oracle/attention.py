@@ -39,14 +39,6 @@ def widen_bf16(bits):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def kv_head_of(h, num_q_heads, num_kv_heads):
-    """Grouped-query mapping: contiguous groups of Hq/Hkv query heads share
-    one KV head (a reading; the pages give no head layout)."""
-    if num_q_heads % num_kv_heads:
-        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
-    return h // (num_q_heads // num_kv_heads)
-
-
 def attend(s, v):
     """Softmax attention of queries over one set of keys, in one pass.
 
@@ -124,20 +116,23 @@ def merge(o, lse):
     M = max_t lse_t: if M = -inf every tile is empty and the result is
     (0, -inf).  Otherwise w_t = exp(lse_t - M) (0 for an empty tile),
     W = sum_t w_t, out = sum_t w_t o_t / W and lse = M + log W.
+    Only lse = -inf marks an empty tile: a NaN log-sum-exp is not a tile
+    the formula can weigh, and IEEE arithmetic of the formula carries it
+    to the row's out and lse (NaN), as it does any NaN input.
     """
     o = np.asarray(o, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)
-    M = lse.max(axis=-1)
-    live = np.isfinite(M)
-    M_safe = np.where(live, M, 0.0)
-    w = np.exp(lse - M_safe[..., None])
-    w = np.where(np.isfinite(lse), w, 0.0)
+    M = lse.max(axis=-1)                       # NaN if any lse of the row is NaN
+    empty_row = M == NEG_INF
+    empty = lse == NEG_INF
+    M_safe = np.where(empty_row, 0.0, M)
+    w = np.where(empty, 0.0, np.exp(lse - M_safe[..., None]))
     W = w.sum(axis=-1)
-    W_safe = np.where(live, W, 1.0)
-    contrib = np.where(np.isfinite(lse)[..., None], w[..., None] * o, 0.0)
+    W_safe = np.where(empty_row, 1.0, W)
+    contrib = np.where(empty[..., None], 0.0, w[..., None] * o)
     out = contrib.sum(axis=-2) / W_safe[..., None]
-    out = np.where(live[..., None], out, 0.0)
-    lse_m = np.where(live, M_safe + np.log(W_safe), NEG_INF)
+    out = np.where(empty_row[..., None], 0.0, out)
+    lse_m = np.where(empty_row, NEG_INF, M_safe + np.log(W_safe))
     return out, lse_m
 
 

@@ -11,21 +11,28 @@
 //
 // Per step, for each active context in the order given, the sink first and
 // then the newest pages downward; a missing page is filled by, in order:
-//   1. one of the context's own pages that fell outside its window;
-//   2. a free page (borrowed if the context already holds its target);
+//   1. one of the context's own pages outside its window (its oldest
+//      non-sink page below the window, or past the end of a history that
+//      got shorter);
+//   2. the lowest-numbered free page, while the context holds fewer than
+//      target + burst (borrowed if it already holds its target);
 //   3. while below target, a page reclaimed from other contexts, least
-//      recently active first: their borrowed pages, then pages above their
-//      (possibly lowered) target, then whole idle contexts;
+//      recently active first (ties: lower id): their borrowed pages, then
+//      pages above their (possibly lowered) target, then whole idle
+//      contexts; a victim gives its oldest non-sink page;
 //   4. the context's own oldest non-sink page older than the one wanted
 //      (shrinking from the oldest, keeping the tail hot);
 // and when none of these exists the context is refused for the step if it
-// lacks its sink or floor, else its window simply stays shorter.  Every fill
-// and reclamation is counted and logged.  No HIP call is made here.
+// lacks its sink or floor, else its window simply stays shorter.  Borrowing
+// is a count per context (never above its pages over target); moving a page
+// inside a context leaves it unchanged.  Every fill and reclamation is
+// counted and logged.  No HIP call is made here.
 #include <algorithm>
 #include <cstdio>
-#include <iterator>
+#include <functional>
 #include <map>
 #include <new>
+#include <queue>
 #include <set>
 #include <vector>
 
@@ -46,7 +53,7 @@ struct Ctx {
   int64_t last_active = 0;      // step it was last active (0 = never)
   std::map<int32_t, int32_t> pages;   // logical page -> device page, oldest first
   std::vector<int32_t> where;         // the same as a dense index (-1: not resident)
-  std::set<int32_t> borrowed;         // device pages held beyond target via burst
+  int32_t borrowed = 0;               // pages held beyond target via burst
   int32_t held() const { return (int32_t)pages.size(); }
   bool has(int32_t lp) const { return lp < (int32_t)where.size() && where[(size_t)lp] >= 0; }
   void put(int32_t lp, int32_t page) {
@@ -61,7 +68,8 @@ struct Ctx {
 struct pkv_admit {
   int64_t num_pages;
   int32_t page_tokens;
-  std::vector<int32_t> free_list;     // LIFO of free device pages
+  // free device pages, lowest first
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_pages;
   std::map<int32_t, Ctx> ctxs;
   int64_t step = 0;
   pkv_admit_counts counts{};
@@ -96,7 +104,12 @@ int32_t drop(Ctx& c, int32_t lp) {
   const int32_t page = it->second;
   c.pages.erase(it);
   c.where[(size_t)lp] = -1;
-  c.borrowed.erase(page);
+  return page;
+}
+
+int32_t pop_free(pkv_admit* A) {
+  const int32_t page = A->free_pages.top();
+  A->free_pages.pop();
   return page;
 }
 
@@ -118,36 +131,38 @@ int32_t oldest_non_sink_below(const Ctx& c, int32_t limit) {
   return (it != c.pages.end() && it->first < limit) ? it->first : -1;
 }
 
-// Oldest non-sink logical page of c holding a borrowed device page, or -1.
-int32_t oldest_borrowed(const Ctx& c) {
-  if (c.borrowed.empty()) return -1;
-  for (auto it = c.pages.upper_bound(0); it != c.pages.end(); ++it)
-    if (c.borrowed.count(it->second)) return it->first;
-  return -1;
+// Oldest non-sink logical page of c outside the window [lo, need), or -1.
+int32_t oldest_outside(const Ctx& c, int32_t lo, int32_t need) {
+  const int32_t below = oldest_non_sink_below(c, lo);
+  if (below >= 0) return below;
+  auto it = c.pages.lower_bound(std::max(need, 1));
+  return it != c.pages.end() ? it->first : -1;
 }
 
 // A page for logical page lp of context c (see the file comment), or -1.
-int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo) {
+int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo, int32_t need) {
   // 1. own page outside the window
-  const int32_t out = oldest_non_sink_below(c, window_lo);
+  const int32_t out = oldest_outside(c, window_lo, need);
   if (out >= 0) {
     const int32_t page = drop(c, out);
     event(A, PKV_ADMIT_REUSE_OWN, c.id, c.id, page, lp);
     return page;
   }
-  // 2. a free page, within target + burst
-  if (!A->free_list.empty() && c.held() < c.target + c.burst) {
-    const int32_t page = A->free_list.back();
-    A->free_list.pop_back();
+  // 2. the lowest free page, within target + burst
+  if (!A->free_pages.empty() && c.held() < c.target + c.burst) {
+    if (c.held() >= c.target) ++c.borrowed;
+    const int32_t page = pop_free(A);
     event(A, PKV_ADMIT_TAKE_FREE, c.id, -1, page, lp);
     return page;
   }
   // 3. reclaim while below target: borrowed, above target, idle contexts
   if (c.held() < c.target) {
     for (Ctx* v : victims_lra(A, c.id)) {
-      const int32_t vl = oldest_borrowed(*v);
+      if (v->borrowed == 0) continue;
+      const int32_t vl = oldest_non_sink_below(*v, INT32_MAX);
       if (vl < 0) continue;
       const int32_t page = drop(*v, vl);
+      --v->borrowed;
       event(A, PKV_ADMIT_RECLAIM_BORROWED, c.id, v->id, page, lp);
       return page;
     }
@@ -161,16 +176,13 @@ int32_t acquire(pkv_admit* A, Ctx& c, int32_t lp, int32_t window_lo) {
     }
     for (Ctx* v : victims_lra(A, c.id)) {
       if (v->last_active == A->step || v->pages.empty()) continue;   // active now, or empty
-      // evict the whole idle context; its pages return to the free list
-      std::vector<int32_t> pages;
-      for (const auto& kv : v->pages) pages.push_back(kv.second);
+      // evict the whole idle context; its pages become free
+      for (const auto& kv : v->pages) A->free_pages.push(kv.second);
       v->pages.clear();
       v->where.clear();
-      v->borrowed.clear();
-      for (auto it = pages.rbegin(); it != pages.rend(); ++it) A->free_list.push_back(*it);
+      v->borrowed = 0;
       event(A, PKV_ADMIT_RECLAIM_IDLE, c.id, v->id, -1, -1);
-      const int32_t page = A->free_list.back();
-      A->free_list.pop_back();
+      const int32_t page = pop_free(A);
       event(A, PKV_ADMIT_TAKE_FREE, c.id, -1, page, lp);
       return page;
     }
@@ -198,8 +210,9 @@ PKV_API int pkv_admit_create(int64_t num_pages, int32_t page_tokens, pkv_admit**
   if (!A) return fail(PKV_ERR_INVALID_ARG, "host allocation failed");
   A->num_pages = num_pages;
   A->page_tokens = page_tokens;
-  A->free_list.reserve((size_t)num_pages);
-  for (int64_t p = num_pages - 1; p >= 0; --p) A->free_list.push_back((int32_t)p);   // 0 first
+  std::vector<int32_t> all((size_t)num_pages);
+  for (int64_t p = 0; p < num_pages; ++p) all[(size_t)p] = (int32_t)p;
+  A->free_pages = decltype(A->free_pages)(std::greater<int32_t>(), std::move(all));
   A->counts.free_pages = num_pages;
   *out = A;
   pkv::clear_error();
@@ -233,8 +246,7 @@ PKV_API int pkv_admit_set_target(pkv_admit* A, int32_t ctx, int32_t target_pages
   c.target = target_pages;   // pages above it become reclaimable
   c.burst = burst_pages;
   // pages held within the new target are held by right, not borrowed
-  while ((int32_t)c.borrowed.size() > std::max(0, c.held() - c.target))
-    c.borrowed.erase(std::prev(c.borrowed.end()));
+  c.borrowed = std::min(c.borrowed, std::max(0, c.held() - c.target));
   pkv::clear_error();
   return PKV_OK;
 }
@@ -243,10 +255,9 @@ PKV_API int pkv_admit_remove(pkv_admit* A, int32_t ctx) {
   if (!A) return fail(PKV_ERR_INVALID_ARG, "admission is NULL");
   auto it = A->ctxs.find(ctx);
   if (it == A->ctxs.end()) return pkv::set_error(PKV_ERR_INVALID_ARG, "no context %d", ctx);
-  for (auto r = it->second.pages.rbegin(); r != it->second.pages.rend(); ++r)
-    A->free_list.push_back(r->second);
+  for (const auto& kv : it->second.pages) A->free_pages.push(kv.second);
   A->ctxs.erase(it);
-  A->counts.free_pages = (int64_t)A->free_list.size();
+  A->counts.free_pages = (int64_t)A->free_pages.size();
   pkv::clear_error();
   return PKV_OK;
 }
@@ -291,7 +302,7 @@ PKV_API int pkv_admit_step(pkv_admit* A, int32_t n, const int32_t* ctx_ids,
     for (int32_t lp = need - 1; lp >= lo; --lp) want.push_back(lp);
     for (int32_t lp : want) {
       if (c.has(lp)) continue;
-      const int32_t page = acquire(A, c, lp, lo);
+      const int32_t page = acquire(A, c, lp, lo, need);
       if (page < 0) {
         if (lp == 0) {
           refused[i] = 1;
@@ -300,7 +311,6 @@ PKV_API int pkv_admit_step(pkv_admit* A, int32_t n, const int32_t* ctx_ids,
         break;
       }
       c.put(lp, page);
-      if (c.held() > c.target) c.borrowed.insert(page);
     }
     if (!refused[i] && c.held() < std::min(kFloor, need)) {
       refused[i] = 1;
@@ -318,7 +328,7 @@ PKV_API int pkv_admit_step(pkv_admit* A, int32_t n, const int32_t* ctx_ids,
     for (int32_t lp = lo_of[i]; lp < need_of[i] && whole; ++lp) whole = row[lp] >= 0;
     status[i] = refused[i] ? PKV_ADMIT_REFUSED_STEP : whole ? PKV_ADMIT_FULL : PKV_ADMIT_PARTIAL;
   }
-  A->counts.free_pages = (int64_t)A->free_list.size();
+  A->counts.free_pages = (int64_t)A->free_pages.size();
   pkv::clear_error();
   return PKV_OK;
 }

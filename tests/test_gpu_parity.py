@@ -153,6 +153,31 @@ def test_merge_identity_and_empty_insertion_bitwise(stress):
         assert same_bits(x, y)
 
 
+@pytest.mark.parametrize("n", [5, 64, 200])
+def test_merge_nan_rows_match_the_oracle(stress, n):
+    """A slot with a NaN log-sum-exp (a flagged partial) makes its row NaN,
+    as the oracle's merge does; rows with only empty slots give (0, -inf);
+    the other rows match the oracle.  Rows of at most 64 slots and longer
+    rows take different merge kernels."""
+    po, pl, _, _ = stress
+    po, pl = po[:, :, :n].clone(), pl[:, :, :n].clone()
+    pl[0, 2, n // 2] = float("nan")          # one flagged slot among live ones
+    pl[1, 5, :] = float("-inf")              # every slot empty
+    pl[1, 6, :] = float("-inf")
+    pl[1, 6, n - 1] = float("nan")           # a flagged slot among empties
+    out, lse = merge(po.contiguous(), pl.contiguous())
+    eo, el = oracle.merge(po.cpu().numpy(), pl.cpu().numpy())
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    nan_rows = np.isnan(el)
+    assert nan_rows[0, 2] and nan_rows[1, 6] and nan_rows.sum() == 2
+    np.testing.assert_array_equal(np.isnan(l), nan_rows)
+    assert np.isnan(o[nan_rows]).all()
+    assert l[1, 5] == -math.inf and (o[1, 5] == 0).all()
+    ok = ~nan_rows
+    assert_out_close(o[ok], eo[ok], tol=1e-4)
+    assert_lse_close(l[ok], el[ok])
+
+
 @pytest.mark.parametrize("n", [1, 2, 17, 63, 64])
 def test_merge_of_one_chunk_matches_two_chunks_bitwise(stress, n):
     """Rows of at most 64 slots are merged as one chunk of slots; the same

@@ -97,6 +97,12 @@ def _merge_no_divide(o, lse):
     return out * W[..., None], l
 
 
+def _merge_nan_as_empty(o, lse):
+    """A NaN log-sum-exp read as an empty tile."""
+    lse = np.asarray(lse, dtype=np.float64)
+    return A.merge(o, np.where(np.isnan(lse), -np.inf, lse))
+
+
 def _one_pass_drop_last(q, k, v, ctx, scale, hkv):
     return A.decode_one_pass(q, k, v, max(ctx - 1, 0), scale, hkv)
 
@@ -136,6 +142,7 @@ MUTANTS = {
     "merge_mean": _mutant(merge=_merge_mean),
     "merge_no_log": _mutant(merge=_merge_no_log),
     "merge_no_divide": _mutant(merge=_merge_no_divide),
+    "merge_nan_as_empty": _mutant(merge=_merge_nan_as_empty),
     "drop_last_key": _mutant(one_pass=_one_pass_drop_last, partials=_partials_drop_last),
     "gqa_modulo": _mutant(one_pass=_one_pass_gqa_modulo),
     "no_scale": _mutant(one_pass=_one_pass_no_scale),
@@ -341,6 +348,29 @@ def pin_merge_algebra(impl):
     np.testing.assert_allclose(l5, lse[:, 0] + math.log(2), atol=1e-14)
 
 
+def pin_nan_propagates(impl):
+    """A NaN log-sum-exp is no empty tile: any NaN operand of the merge's
+    sums and maximum makes them NaN in IEEE arithmetic, so the row's out and
+    lse are NaN; the other rows equal their merge without that row, and an
+    all-empty row stays (0, -inf)."""
+    g = np.random.default_rng(23)
+    o = g.standard_normal((4, 6, 10))
+    lse = g.uniform(-20, 20, size=(4, 6))
+    lse[1, 3] = np.nan
+    lse[2, :] = -np.inf
+    o[2] = 0.0
+    lse[3, 0] = np.nan
+    lse[3, 1:] = -np.inf
+    out, l = impl.merge(o, lse)
+    for r in (1, 3):
+        assert np.isnan(l[r]) and np.isnan(out[r]).all(), r
+    assert l[2] == -np.inf and (out[2] == 0).all()
+    o0, l0 = impl.merge(o[:1], lse[:1])
+    np.testing.assert_array_equal(out[0], o0[0])
+    np.testing.assert_array_equal(l[0], l0[0])
+    assert np.isfinite(l[0]) and np.isfinite(out[0]).all()
+
+
 def pin_stress_construction(impl):
     """Partials built from explicit keys merge to softmax over all those keys."""
     from paged_kv_cache_10_amd import inputs
@@ -368,7 +398,8 @@ def pin_stress_construction(impl):
 
 
 PINS = [pin_golden_attention, pin_golden_merge, pin_brute_force, pin_library, pin_closed_forms,
-        pin_shift_and_permutation, pin_tiling_invariance, pin_merge_algebra, pin_stress_construction]
+        pin_shift_and_permutation, pin_tiling_invariance, pin_merge_algebra, pin_nan_propagates,
+        pin_stress_construction]
 
 
 # ----------------------------------------------------------------------------
