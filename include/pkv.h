@@ -262,6 +262,31 @@ int pkv_decode_attention_merged(const pkv_pool* pool, int32_t layer, const void*
                                 float* lse, void* workspace, uint64_t workspace_bytes,
                                 const pkv_decode_opts* opts, void* stream);
 
+/* The same call for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Identical to pkv_decode_attention_merged (same kernels, same bits) except
+ * that the split partials of a tile with several splits live in a static
+ * device buffer of the library, PKV_STATIC_SCRATCH_BYTES (16 MiB) per GPU,
+ * which the library holds from its first use on that GPU until the process
+ * ends, instead of a caller workspace.  The call itself allocates nothing
+ * (no hipMalloc, no allocating library routine).  A call needing more than
+ * that (pkv_decode_workspace_bytes) is refused with PKV_ERR_WORKSPACE; one
+ * needing none (opts.split_tokens = tile_tokens, or the default split equal
+ * to the tile) never touches the buffer.  Every call on one GPU shares the
+ * buffer and finds the last call's contents in it (nothing in it needs a
+ * start value): two calls that may run at the same time on one GPU (on
+ * different streams, or from different threads) race, so order them on one
+ * stream.  Other arguments, outputs and errors as
+ * pkv_decode_attention_merged. */
+#define PKV_STATIC_SCRATCH_BYTES (16ull << 20)
+int pkv_decode_attention_merged_noalloc(const pkv_pool* pool, int32_t layer, const void* q,
+                                        const int32_t* dev_table, int32_t pt_stride,
+                                        const int32_t* dev_ctx_lens, int32_t batch,
+                                        int32_t num_q_heads, int32_t token_count,
+                                        int32_t tile_tokens, float scale, float* part_out,
+                                        float* part_lse, int32_t num_slots, float* out,
+                                        float* lse, const pkv_decode_opts* opts, void* stream);
+
 /* ---------------------------------------------------- runs in one launch --
  * The runs of two representations (KV-cache engineering, section "Exact
  * recent pages, compact older pages": a compact older run and an exact

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -528,6 +529,68 @@ PKV_API int pkv_decode_attention_merged(const pkv_pool* pool, int32_t layer, con
   return decode_impl(pool, layer, q, dev_table, pt_stride, dev_ctx_lens, batch, num_q_heads, 0,
                      token_count, tile_tokens, scale, part_out, part_lse, num_slots, workspace,
                      workspace_bytes, opts, stream, out, lse);
+}
+
+// Device scratch for pkv_decode_attention_merged_noalloc: a file-scope
+// array, one copy per GPU the library runs on, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is a
+// stand-in, not a device pointer): each device's address is looked up once
+// with hipGetSymbolAddress, with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address (the current device's), or an error code.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_DEVICE, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+PKV_API int pkv_decode_attention_merged_noalloc(const pkv_pool* pool, int32_t layer,
+                                                const void* q, const int32_t* dev_table,
+                                                int32_t pt_stride, const int32_t* dev_ctx_lens,
+                                                int32_t batch, int32_t num_q_heads,
+                                                int32_t token_count, int32_t tile_tokens,
+                                                float scale, float* part_out, float* part_lse,
+                                                int32_t num_slots, float* out, float* lse,
+                                                const pkv_decode_opts* opts, void* stream) {
+  if (!out || !lse) return fail(PKV_ERR_INVALID_ARG, "out or lse is NULL");
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  uint64_t need = 0;
+  if (int rc = pkv_decode_workspace_bytes(batch, num_q_heads, pool->geom.head_dim, token_count,
+                                          tile_tokens, opts, &need))
+    return rc;
+  if (need > PKV_STATIC_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "this call needs %llu bytes of split partials; the static scratch holds %llu "
+                "(PKV_STATIC_SCRATCH_BYTES): use pkv_decode_attention_merged with a workspace, "
+                "or fewer splits per tile (opts.split_tokens = tile_tokens needs none)",
+                (unsigned long long)need, (unsigned long long)PKV_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0)
+    if (int rc = scratch_for_current_device(&ws)) return rc;
+  return decode_impl(pool, layer, q, dev_table, pt_stride, dev_ctx_lens, batch, num_q_heads, 0,
+                     token_count, tile_tokens, scale, part_out, part_lse, num_slots, ws,
+                     need > 0 ? (uint64_t)PKV_STATIC_SCRATCH_BYTES : 0, opts, stream, out, lse);
 }
 
 PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batch,

@@ -33,6 +33,7 @@ EXPORTS = [
     "pkv_compact_page_bytes", "pkv_compact_pool_create", "pkv_pool_format",
     "pkv_compact_convert", "pkv_compact_crc", "pkv_plan_tiles", "pkv_decode_attention_rows",
     "pkv_decode_attention_merged", "pkv_decode_attention_runs",
+    "pkv_decode_attention_merged_noalloc",
 ]
 
 
@@ -123,6 +124,9 @@ def lib():
         L.pkv_decode_attention_merged.argtypes = [P, I32, P, P, I32, P, I32, I32, I32, I32,
                                                   ctypes.c_float, P, P, I32, P, P, P, U64,
                                                   ctypes.POINTER(DecodeOpts), P]
+        L.pkv_decode_attention_merged_noalloc.argtypes = [P, I32, P, P, I32, P, I32, I32, I32,
+                                                          I32, ctypes.c_float, P, P, I32, P, P,
+                                                          ctypes.POINTER(DecodeOpts), P]
         L.pkv_plan_tiles.argtypes = [I32P, I32, I32, I32, I32, I32P, I32P]
         L.pkv_decode_attention_runs.argtypes = [I32, P, I32, I32, ctypes.POINTER(DecodeRun), I32,
                                                 ctypes.c_float, P, P, I32, P]
@@ -330,6 +334,35 @@ def decode_attention_merged(pool, layer, q, dev_table, dev_ctx_lens, token_count
         int(tile_tokens), float(scale), _ptr(part_out, torch.float32, "part_out"),
         _ptr(part_lse, torch.float32, "part_lse"), num_slots, _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def decode_attention_merged_noalloc(pool, layer, q, dev_table, dev_ctx_lens, token_count,
+                                    tile_tokens, scale, part_out, part_lse, out, lse, kernel=0,
+                                    split_tokens=0, stream=None):
+    """decode_attention_merged with the library's static device scratch in
+    place of a workspace (pkv_decode_attention_merged_noalloc)."""
+    import torch
+    B, Hq, D = q.shape
+    if part_out.dim() != 4 or part_out.shape[:2] != (B, Hq) or part_out.shape[3] != D:
+        raise ValueError("part_out must be [B, Hq, num_slots, D]")
+    num_slots = part_out.shape[2]
+    if tuple(part_lse.shape) != (B, Hq, num_slots):
+        raise ValueError("part_lse must be [B, Hq, num_slots]")
+    if tuple(out.shape) != (B, Hq, D) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out must be [B, Hq, D] and lse [B, Hq]")
+    if dev_table.dim() != 2 or dev_table.shape[0] != B or dev_table.stride(1) != 1:
+        raise ValueError("dev_table must be [B, pt_stride] with contiguous rows")
+    o = _opts(kernel, split_tokens, 0)
+    _check(lib().pkv_decode_attention_merged_noalloc(
+        pool.handle, int(layer), _ptr(q, torch.bfloat16, "q"),
+        dev_table.data_ptr(), int(dev_table.stride(0)),
+        _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"), B, Hq, int(token_count),
+        int(tile_tokens), float(scale), _ptr(part_out, torch.float32, "part_out"),
+        _ptr(part_lse, torch.float32, "part_lse"), num_slots, _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), ctypes.byref(o), _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 16 << 20     # PKV_STATIC_SCRATCH_BYTES
 
 
 def decode_attention_runs(layer, q, runs, scale, part_out, part_lse, stream=None):

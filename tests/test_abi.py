@@ -184,6 +184,26 @@ def test_decode_arguments_are_refused_on_the_host(kw, code, needle):
     assert rc == code and needle in msg, msg
 
 
+def test_noalloc_decode_refuses_more_than_its_static_scratch():
+    """pkv_decode_attention_merged_noalloc refuses, on the host and before
+    touching any device, a call whose split partials exceed the library's
+    static scratch; a call with nothing to do returns without touching it."""
+    L = pkv.lib()
+    pool = FakePool(64)
+
+    def call(batch, count, tile, split):
+        o = pkv.DecodeOpts(0, split)
+        return L.pkv_decode_attention_merged_noalloc(
+            pool.handle, 0, 1 << 20, 1 << 21, count // 64, 1 << 22, batch, 24, count, tile,
+            0.0625, 1 << 23, 1 << 24, count // tile, 1 << 25, 1 << 26, ctypes.byref(o), None)
+
+    # 64 requests x 24 heads x 64 splits x 257 floats = 101 MB > 16 MiB
+    assert call(64, 262144, 262144, 4096) == -4
+    assert "PKV_STATIC_SCRATCH_BYTES" in err()
+    assert pkv.STATIC_SCRATCH_BYTES == 16 << 20
+    assert call(0, 262144, 262144, 4096) == 0          # no request: nothing launched
+
+
 def test_merge_arguments_are_refused_on_the_host():
     L = pkv.lib()
     assert L.pkv_merge_partials(1 << 20, 1 << 21, 4, 0, 256, 1 << 22, 1 << 23, None) == -1
