@@ -536,6 +536,94 @@ int pkv_admit_get_counts(const pkv_admit* a, pkv_admit_counts* out);
 int pkv_admit_events(pkv_admit* a, pkv_admit_event* out, int32_t cap, int32_t* n_out);
 int pkv_admit_destroy(pkv_admit* a);
 
+/* ------------------------------------------------------------ live pool --
+ * Decode steps over histories whose authoritative copy is in pinned host
+ * memory, with a device pool smaller than the histories (Staging without a
+ * stall, sections "Admission that does arithmetic", "Two copy queues and
+ * device-side ordering" and "Leases instead of buffers"; GPU memory
+ * management, sections "Pages held by right, borrowed or free" and "Staging
+ * as a lease").  Each step the admission planner above (the runtime owns
+ * one, over the pool's pages) decides which logical pages of each context
+ * hold pool pages: the sink and the newest pages.  A pool page that turns
+ * hot (it now serves a (context, logical page) whose bytes it does not
+ * hold) is copied in from the host once; every other logical page of the
+ * history is staged, one layer at a time, into the staging pool.  One
+ * decode launch per layer reads both through a composed table, so a step's
+ * partials, out and lse are bit-identical to pkv_decode_attention_merged of
+ * a fully resident copy of the same histories at the same tile_tokens and
+ * split (a tile's arithmetic depends only on its logical tokens).  The new
+ * token is appended on the device and only its rows are written back to the
+ * host pages (2 x num_kv_heads x 256 bf16 per context and layer).
+ *
+ * The composed table (device int32, inside dev_state): entry i of row b is
+ * the pool page of logical page i if resident, else num_pages(pool) + s for
+ * staging page s; -1 past the history.
+ *
+ * pkv_live_create
+ *   pool        bf16 pool of L layers whose pages admission hands out.
+ *   stage       bf16 pool, same KV heads; its num_layers K is the number of
+ *               staging buffers (layer l stages into its layer l % K) and
+ *               its num_pages the most pages one step may stage (a step that
+ *               stages more fails and quarantines the runtime).
+ *   host_arena  pinned host memory the device can address (hipHostMalloc),
+ *               the layout of an L-layer pool: host[layer][page][K|V]
+ *               [kv_head][block]; host_bytes a whole number of such pages.
+ *   max_batch   contexts per step, at most; pt_stride: pages per table row.
+ *   dev_state   device int32 [max_batch * (pt_stride + 2)], the caller's:
+ *               the step's composed table, lengths and append positions.
+ *   streams     copy (host -> device pages), compute (table copy, append,
+ *               decode, merge) and write-back (new rows -> host), the
+ *               caller's, default priority.
+ *   The runtime allocates a pinned ring of 4 step tables (host memory, at
+ *   create) and never device memory.
+ * pkv_live_add / pkv_live_set_target / pkv_live_remove: contexts, with the
+ *   target / burst / floor of pkv_admit_*.  pkv_live_admission gives the
+ *   runtime's planner for pkv_admit_get_counts / pkv_admit_events only.
+ * pkv_live_step_begin: n contexts (priority order) with their lengths in
+ *   tokens including this step's new token, and host_rows [n][host_stride]:
+ *   the host page of each logical page.  Fills status [n] (PKV_ADMIT_FULL,
+ *   _PARTIAL, _REFUSED_STEP; a refused context decodes nothing, out 0 and
+ *   lse -inf, and is not appended) and *info (may be NULL).  Runs admission,
+ *   composes the table and queues its copy on the compute stream; waits on
+ *   the host only when the ring is full (the GPU 4 steps behind).  Refused
+ *   with PKV_ERR_LEASE while the previous step has a layer not yet run.
+ * pkv_live_layer: one layer of the open step, each layer once.  On the copy
+ *   stream, after the previous step's write-back of this layer and the last
+ *   reader of the staging buffer: the hot pages' and staged pages' slices
+ *   of this layer.  On the compute stream: k_new / v_new ([n][Hkv][256]
+ *   bf16, 16-byte aligned) appended at position length - 1, then
+ *   pkv_decode_attention_merged over the composed table with token_count =
+ *   num_slots x tile_tokens (every length must fit) into part_out,
+ *   part_lse, out, lse ([n][num_q_heads]...).  On the write-back stream,
+ *   after the decode: the new rows into the host pages.  Arguments are
+ *   checked before anything is queued.
+ * pkv_live_destroy waits for the three streams, then frees host state.  A
+ *   HIP failure quarantines the runtime: every call but destroy is refused.
+ */
+typedef struct pkv_live pkv_live;
+typedef struct pkv_live_info {
+  int64_t copied_in_pages;  /* pool pages filled from the host this step (every layer) */
+  int64_t staged_pages;     /* pages staged for each layer this step */
+  int32_t refused;          /* contexts refused this step */
+  int32_t resident_pages;   /* pool pages the step reads */
+} pkv_live_info;
+int pkv_live_create(const pkv_pool* pool, const pkv_pool* stage, void* host_arena,
+                    uint64_t host_bytes, int32_t max_batch, int32_t pt_stride, int32_t* dev_state,
+                    void* copy_stream, void* compute_stream, void* writeback_stream,
+                    pkv_live** out);
+int pkv_live_add(pkv_live* live, int32_t ctx, int32_t target_pages, int32_t burst_pages);
+int pkv_live_set_target(pkv_live* live, int32_t ctx, int32_t target_pages, int32_t burst_pages);
+int pkv_live_remove(pkv_live* live, int32_t ctx);
+int pkv_live_admission(pkv_live* live, pkv_admit** out);
+int pkv_live_step_begin(pkv_live* live, int32_t n, const int32_t* ctx_ids, const int64_t* lengths,
+                        const int32_t* host_rows, int32_t host_stride, int32_t* status,
+                        pkv_live_info* info);
+int pkv_live_layer(pkv_live* live, int32_t layer, const void* q, const void* k_new,
+                   const void* v_new, int32_t num_q_heads, int32_t tile_tokens, float scale,
+                   float* part_out, float* part_lse, int32_t num_slots, float* out, float* lse,
+                   void* workspace, uint64_t workspace_bytes, const pkv_decode_opts* opts);
+int pkv_live_destroy(pkv_live* live);
+
 #ifdef __cplusplus
 }
 #endif

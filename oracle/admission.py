@@ -31,14 +31,15 @@ notes):
   R2  Within a step, contexts are served in the order given.  A context
       wants its sink first, then its window pages from the newest down; the
       first page it cannot fill ends its turn.
-  R3  "Own page outside the window": the context's oldest non-sink page
-      outside [lo, n) moves to the wanted logical page (below lo in a
-      growing history; past the end only if the history got shorter).
-  R4  "Free page": the lowest-numbered free device page, taken only while
+  R3  Reuse of a page of its own that lies outside its window: the oldest
+      such non-sink page (outside [lo, n): below lo in a growing history,
+      past the end only if the history got shorter) moves to the wanted
+      logical page.
+  R4  A free page: the lowest-numbered free device page, taken only while
       the context holds fewer than target + burst pages.  Taken while it
       already holds its target or more, the page is borrowed: the
       context's borrowed count rises by one.
-  R5  "Reclaim within the target": only a context holding fewer pages than
+  R5  Reclamation inside the target: only a context holding fewer pages than
       its target reclaims.  Victims are the other contexts ordered by the
       step they were last active (earliest first; never active counts as
       step 0), ties by lower context id.  First pass: the first victim with
@@ -48,8 +49,9 @@ notes):
       victim not active in this step that holds any page is evicted whole
       (all its pages become free, its borrowed count 0), then R4's lowest
       free page is taken.
-  R6  "Shrink from the oldest page while keeping the tail hot": the
-      context's own oldest non-sink page below the wanted page moves to it.
+  R6  Shrinking from its oldest end so that its newest pages stay
+      resident: the context's own oldest non-sink page below the wanted
+      page moves to it.
   R7  A context that cannot get its sink is refused for the step; so is one
       left holding fewer than min(2, n) pages (its floor).  Otherwise a
       window that could not be filled stays short: status partial.

@@ -26,7 +26,7 @@ C_ABI_SRC = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "decode_from_c
 C_ABI_EXE = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "decode_from_c")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "stager.cpp", "admit.cpp", "merge.hip", "decode_valu.hip", "decode_mfma.hip", "append.hip", "compact.hip", "decode_fp8.hip", "decode_runs.hip"]
+SOURCES = ["api.cpp", "stager.cpp", "admit.cpp", "live.cpp", "merge.hip", "decode_valu.hip", "decode_mfma.hip", "append.hip", "compact.hip", "decode_fp8.hip", "decode_runs.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

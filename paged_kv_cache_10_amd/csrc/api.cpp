@@ -321,13 +321,16 @@ PKV_API int pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
 namespace {
 
 // pkv_decode_attention, and with fin_out / fin_lse also the final merge of
-// every slot of each row (pkv_decode_attention_merged).
+// every slot of each row (pkv_decode_attention_merged).  With `stage`,
+// table entries past the pool's pages name pages of a staging pool's layer
+// (the live pool's composed tables; the MFMA kernel only).
 int decode_impl(const pkv_pool* pool, int32_t layer, const void* q, const int32_t* dev_table,
                 int32_t pt_stride, const int32_t* dev_ctx_lens, int32_t batch,
                 int32_t num_q_heads, int32_t token_begin, int32_t token_count,
                 int32_t tile_tokens, float scale, float* part_out, float* part_lse,
                 int32_t num_slots, void* workspace, uint64_t workspace_bytes,
-                const pkv_decode_opts* opts, void* stream, float* fin_out, float* fin_lse) {
+                const pkv_decode_opts* opts, void* stream, float* fin_out, float* fin_lse,
+                const pkv::StageRef* stage = nullptr, bool dry_run = false) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   const pkv_geom& G = pool->geom;
   if (layer < 0 || layer >= G.num_layers)
@@ -401,6 +404,10 @@ int decode_impl(const pkv_pool* pool, int32_t layer, const void* q, const int32_
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16)
     return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
+  if (stage && (kernel != 2 || pool->format != PKV_FORMAT_BF16))
+    return fail(PKV_ERR_INVALID_ARG, "staged pages are read by the MFMA kernel from bf16 pools");
+  if (dry_run) return ok();
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   pkv::DecodeArgs a;
   a.arena = static_cast<const uint16_t*>(pool->base);
@@ -418,6 +425,12 @@ int decode_impl(const pkv_pool* pool, int32_t layer, const void* q, const int32_
   a.split_tokens = split;
   a.row_split = nullptr;
   a.scale_log2 = scale * pkv::kLog2e;
+  if (stage) {
+    a.stage_arena = static_cast<const uint16_t*>(stage->pool->base);
+    a.stage_layer_off = (int64_t)(stage->pool->page_layer_bytes / 2) * stage->pool->num_pages *
+                        stage->layer;
+    a.stage_pages = (int32_t)stage->pool->num_pages;
+  }
 
   const int n_split = token_count / split;
   float* ws_o = nullptr;
@@ -504,6 +517,21 @@ int decode_impl(const pkv_pool* pool, int32_t layer, const void* q, const int32_
 }
 
 }  // namespace
+
+namespace pkv {
+int decode_merged_staged(const pkv_pool* pool, int32_t layer, const void* q,
+                         const int32_t* dev_table, int32_t pt_stride, const int32_t* dev_ctx_lens,
+                         int32_t batch, int32_t num_q_heads, int32_t token_count,
+                         int32_t tile_tokens, float scale, float* part_out, float* part_lse,
+                         int32_t num_slots, float* out, float* lse, void* workspace,
+                         uint64_t workspace_bytes, const pkv_decode_opts* opts, void* stream,
+                         const StageRef& stage, bool dry_run) {
+  if (!out || !lse) return fail(PKV_ERR_INVALID_ARG, "out or lse is NULL");
+  return decode_impl(pool, layer, q, dev_table, pt_stride, dev_ctx_lens, batch, num_q_heads, 0,
+                     token_count, tile_tokens, scale, part_out, part_lse, num_slots, workspace,
+                     workspace_bytes, opts, stream, out, lse, &stage, dry_run);
+}
+}  // namespace pkv
 
 PKV_API int pkv_decode_attention(const pkv_pool* pool, int32_t layer, const void* q,
                                  const int32_t* dev_table, int32_t pt_stride,

@@ -239,12 +239,20 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const WorkItem
     qv[r] = (h < G) ? reinterpret_cast<const uint4*>(a.q + (row0 + h) * D)[i % (D / 8)]
                     : make_uint4(0, 0, 0, 0);
   }
+  const uint16_t* stage_base = a.stage_arena + a.stage_layer_off;
   auto page_at = [&](int j) {
     PageRef pg;
     int phys = __builtin_amdgcn_readlane(my_id, j);
     pg.valid = min(PT, t1 - (t0 + (w + kWaves * j) * PT));
-    if (phys < 0 || phys >= a.num_pages) { phys = 0; pg.valid = 0; }   // read page 0, mask all
-    const uint16_t* page = layer_base + (int64_t)phys * a.page_elems;
+    const uint16_t* base = layer_base;
+    if (phys >= a.num_pages && phys - a.num_pages < a.stage_pages) {   // a staged page
+      phys -= a.num_pages;
+      base = stage_base;
+    } else if (phys < 0 || phys >= a.num_pages) {
+      phys = 0;                                    // read page 0 of the pool, mask all
+      pg.valid = 0;
+    }
+    const uint16_t* page = base + (int64_t)phys * a.page_elems;
     pg.k = page + (int64_t)g * PT * D;
     pg.v = page + (int64_t)(a.num_kv_heads + g) * PT * D;
     return pg;

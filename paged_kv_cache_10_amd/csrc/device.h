@@ -305,6 +305,13 @@ struct DecodeArgs {
   float* out_lse;            // [batch][num_q_heads][out_slots]
   int32_t out_slots;         // slots per row of out_o / out_lse
   int32_t out_slot0;         // slot written by split 0 of this window
+  // A second, staging arena (the MFMA kernel only): a table entry e with
+  // num_pages <= e < num_pages + stage_pages names page e - num_pages of it,
+  // read from stage_arena + stage_layer_off; every other entry outside
+  // [0, num_pages) is skipped.  stage_pages = 0: no staging arena.
+  const uint16_t* stage_arena = nullptr;
+  int64_t stage_layer_off = 0;
+  int32_t stage_pages = 0;
 };
 
 }  // namespace pkv

@@ -428,3 +428,37 @@ def stress_draws(seed=5, batch=64, heads=24, tiles=256, keys=4, dim=256,
         empty[0, 1, :] = True
         empty[0, 1, tiles // 2] = False
     return dict(r=r, vals=vals, target_lse=target, empty=empty)
+
+
+# ----------------------------------------------------------------------------
+# a live-pool schedule: the 4-request shape growing by one token per step in
+# a device pool smaller than the histories
+
+
+def live_schedule(steps=20):
+    """Four requests of about 31,744 tokens, each growing by one token per
+    step it takes part in (the new token counts in the step's length; a
+    paused request keeps its length), served from a device
+    pool of 1,491 pages, three quarters of the 1,988 pages the final
+    histories fill.  The starting lengths differ by a few tokens, so the
+    requests open their 497th page at different steps.  Targets and bursts
+    (pages) change mid-run and one request pauses for a step, so that every
+    source of a page is used: reuse of an own page, free pages, borrowed,
+    above-target and idle reclamation, and shrinking.
+
+    Returns dict(pool_pages, start [4], contexts {id: (target, burst)},
+    steps [list of dict(ids, lengths, set_target {id: (target, burst)})],
+    final [4]).  Lengths are tokens including the step's new token."""
+    start = [31744 - 9, 31744 - 5, 31744 - 13, 31744 - 1]
+    contexts = {0: (300, 200), 1: (300, 200), 2: (400, 0), 3: (380, 0)}
+    retarget = {8: {2: (300, 0), 0: (600, 0)}, 12: {1: (500, 0)}}
+    paused = {12: {3}}
+    plan = []
+    length = list(start)
+    for s in range(1, steps + 1):
+        ids = [c for c in range(4) if c not in paused.get(s, set())]
+        for c in ids:
+            length[c] += 1
+        plan.append(dict(ids=ids, lengths=[length[c] for c in ids],
+                         set_target=retarget.get(s, {})))
+    return dict(pool_pages=1491, start=start, contexts=contexts, steps=plan, final=length)

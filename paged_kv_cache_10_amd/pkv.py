@@ -34,6 +34,8 @@ EXPORTS = [
     "pkv_compact_convert", "pkv_compact_crc", "pkv_plan_tiles", "pkv_decode_attention_rows",
     "pkv_decode_attention_merged", "pkv_decode_attention_runs",
     "pkv_decode_attention_merged_noalloc",
+    "pkv_live_create", "pkv_live_add", "pkv_live_set_target", "pkv_live_remove",
+    "pkv_live_admission", "pkv_live_step_begin", "pkv_live_layer", "pkv_live_destroy",
 ]
 
 
@@ -152,6 +154,16 @@ def lib():
         L.pkv_admit_get_counts.argtypes = [P, ctypes.POINTER(AdmitCounts)]
         L.pkv_admit_events.argtypes = [P, ctypes.POINTER(AdmitEvent), I32, ctypes.POINTER(I32)]
         L.pkv_admit_destroy.argtypes = [P]
+        L.pkv_live_create.argtypes = [P, P, P, U64, I32, I32, P, P, P, P, ctypes.POINTER(P)]
+        L.pkv_live_add.argtypes = [P, I32, I32, I32]
+        L.pkv_live_set_target.argtypes = [P, I32, I32, I32]
+        L.pkv_live_remove.argtypes = [P, I32]
+        L.pkv_live_admission.argtypes = [P, ctypes.POINTER(P)]
+        L.pkv_live_step_begin.argtypes = [P, I32, I32P, I64P, I32P, I32, I32P,
+                                          ctypes.POINTER(LiveInfo)]
+        L.pkv_live_layer.argtypes = [P, I32, P, P, P, I32, I32, ctypes.c_float, P, P, I32, P, P,
+                                     P, U64, ctypes.POINTER(DecodeOpts)]
+        L.pkv_live_destroy.argtypes = [P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -526,11 +538,15 @@ class Stager:
 class Admission:
     """Host-side device page admission (pkv_admit_*)."""
 
-    def __init__(self, num_pages, page_tokens=64):
+    def __init__(self, num_pages, page_tokens=64, _borrowed=None):
+        if _borrowed is not None:          # a planner owned by a live pool: never destroyed here
+            self.handle, self.num_pages, self._owned = _borrowed, num_pages, False
+            return
         h = P()
         _check(lib().pkv_admit_create(int(num_pages), int(page_tokens), ctypes.byref(h)))
         self.handle = h
         self.num_pages = num_pages
+        self._owned = True
 
     def add(self, ctx, target, burst=0):
         _check(lib().pkv_admit_add(self.handle, ctx, target, burst))
@@ -573,15 +589,110 @@ class Admission:
                 return out
 
     def close(self):
-        if getattr(self, "handle", None):
+        if getattr(self, "handle", None) and getattr(self, "_owned", True):
             lib().pkv_admit_destroy(self.handle)
-            self.handle = None
+        self.handle = None
 
     def __del__(self):
         try:
             self.close()
         except Exception:
             pass
+
+
+class LiveInfo(ctypes.Structure):
+    _fields_ = [("copied_in_pages", ctypes.c_int64), ("staged_pages", ctypes.c_int64),
+                ("refused", ctypes.c_int32), ("resident_pages", ctypes.c_int32)]
+
+
+class Live:
+    """The live pool (pkv_live_*): histories in the pinned host tensor
+    `host_arena` (pool layout, the pool's layers), device pages of `pool`
+    admitted per step, the rest staged into `stage_pool` (its layers are the
+    staging buffers), one decode over a composed table per layer."""
+
+    def __init__(self, pool, stage_pool, host_arena, max_batch, pt_stride, copy_stream,
+                 compute_stream, writeback_stream):
+        import torch
+        if not host_arena.is_pinned():
+            raise ValueError("host_arena must be pinned host memory")
+        self.pool, self.stage_pool, self.host_arena = pool, stage_pool, host_arena
+        self.max_batch, self.pt_stride = max_batch, pt_stride
+        self.streams = (copy_stream, compute_stream, writeback_stream)
+        self.dev_state = torch.full((max_batch * (pt_stride + 2),), -1, dtype=torch.int32,
+                                    device="cuda")
+        h = P()
+        _check(lib().pkv_live_create(pool.handle, stage_pool.handle, host_arena.data_ptr(),
+                                     host_arena.numel() * host_arena.element_size(), max_batch,
+                                     pt_stride, self.dev_state.data_ptr(), _stream(copy_stream),
+                                     _stream(compute_stream), _stream(writeback_stream),
+                                     ctypes.byref(h)))
+        self.handle = h
+        a = P()
+        _check(lib().pkv_live_admission(self.handle, ctypes.byref(a)))
+        self.admission = Admission(pool.num_pages, _borrowed=a)
+
+    def add(self, ctx, target, burst=0):
+        _check(lib().pkv_live_add(self.handle, ctx, target, burst))
+
+    def set_target(self, ctx, target, burst=0):
+        _check(lib().pkv_live_set_target(self.handle, ctx, target, burst))
+
+    def remove(self, ctx):
+        _check(lib().pkv_live_remove(self.handle, ctx))
+
+    def begin(self, ctx_ids, lengths, host_rows):
+        """Open a step: lengths include the new token; host_rows int32
+        [n, stride] host pages.  Returns (status list, info dict)."""
+        import numpy as np
+        ids, idp = _i32_array(ctx_ids)
+        ln = np.ascontiguousarray(lengths, dtype=np.int64)
+        hr, hp = _i32_array(host_rows)
+        n = len(ids)
+        if hr.shape[0] != n:
+            raise ValueError("host_rows must have one row per context")
+        status = np.empty(max(n, 1), dtype=np.int32)
+        info = LiveInfo()
+        _check(lib().pkv_live_step_begin(self.handle, n, idp,
+                                         ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), hp,
+                                         hr.shape[1], status.ctypes.data_as(I32P),
+                                         ctypes.byref(info)))
+        return ([ADMIT_STATUS[int(x)] for x in status[:n]],
+                {k: getattr(info, k) for k, _ in LiveInfo._fields_})
+
+    def layer(self, layer, q, k_new, v_new, tile_tokens, scale, part_out, part_lse, out, lse,
+              workspace=None, split_tokens=0):
+        import torch
+        n, Hq, D = q.shape
+        num_slots = part_out.shape[2]
+        if tuple(part_out.shape) != (n, Hq, num_slots, D) or tuple(part_lse.shape) != (n, Hq, num_slots):
+            raise ValueError("part_out must be [n, Hq, num_slots, D] and part_lse [n, Hq, num_slots]")
+        if tuple(out.shape) != (n, Hq, D) or tuple(lse.shape) != (n, Hq):
+            raise ValueError("out must be [n, Hq, D] and lse [n, Hq]")
+        if k_new.shape[0] != n or v_new.shape != k_new.shape:
+            raise ValueError("k_new and v_new must be [n, Hkv, D]")
+        o = _opts(0, split_tokens, 0)
+        ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib().pkv_live_layer(self.handle, int(layer), _ptr(q, torch.bfloat16, "q"),
+                                    _ptr(k_new, torch.bfloat16, "k_new"),
+                                    _ptr(v_new, torch.bfloat16, "v_new"), Hq, int(tile_tokens),
+                                    float(scale), _ptr(part_out, torch.float32, "part_out"),
+                                    _ptr(part_lse, torch.float32, "part_lse"), num_slots,
+                                    _ptr(out, torch.float32, "out"),
+                                    _ptr(lse, torch.float32, "lse"), ws_ptr, ws_bytes,
+                                    ctypes.byref(o)))
+
+    def table(self, n):
+        """The open step's composed table, lengths and positions (device)."""
+        t = self.dev_state[:self.max_batch * self.pt_stride].view(self.max_batch, self.pt_stride)
+        lens = self.dev_state[self.max_batch * self.pt_stride:][:self.max_batch]
+        return t[:n], lens[:n]
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            _check(lib().pkv_live_destroy(self.handle))
+            self.handle = None
 
 
 def pool_format(pool):
