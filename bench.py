@@ -230,6 +230,9 @@ def parse():
     ap.add_argument("--merge-stress", action="store_true",
                     help="time pkv_merge_partials alone on 64 x 24 rows x 256 partials; "
                          "prints its own JSON line")
+    ap.add_argument("--live", action="store_true",
+                    help="the live pool: four ~31,744-token requests growing by one token per "
+                         "step, device pool 3/4 of the pages, histories in pinned host memory")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the timed step in a HIP graph and time its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,6 +254,9 @@ def main():
     ceiling = None if args.no_read_probe else read_probe()
     if args.merge_stress:
         print(json.dumps(merge_stress(args, ceiling)), flush=True)
+        return 0
+    if args.live:
+        print(json.dumps(live_pool(args)), flush=True)
         return 0
     import torch
     from paged_kv_cache_10_amd import inputs as I
@@ -651,6 +657,176 @@ def host_staged(args, w, pool, arena, table, ctx, qs, ref_outs, ref_lses, T, spa
                      "frac": round(copied / (ms * 1e-3) / 1e9 / h2d_ceiling, 4),
                      "peak_kind": "measured: plain 1 GiB pinned-to-device copy (faster of one "
                                   "copy and two halves on two streams)"},
+    }
+
+
+def live_pool(args):
+    """The live pool (pkv_live_*) on the 4-request shape: each history in
+    pinned host memory (contiguous per layer), a device pool of 1,491 pages
+    (3/4 of the histories' pages), admission per step, hot pages copied in,
+    the rest staged per layer, the new token appended and its rows written
+    back, one decode over the composed table per layer.  First the 20-step
+    schedule of the GPU test (targets change, a request pauses), every layer
+    checked bitwise against a resident decode; then `steps` timed steps with
+    all four requests growing, against the resident decode of the same
+    histories."""
+    import torch
+    from paged_kv_cache_10_amd import inputs as I
+    from paged_kv_cache_10_amd import pkv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sc = I.live_schedule(20)
+    grow = args.warmup + args.steps
+    final = [f + grow for f in sc["final"]]
+    W = I.Workload("live", seed=81, ctx_lens=final, num_layers=16, tile_tokens=8192)
+    L, Hq, Hkv, D, PT = W.num_layers, W.num_q_heads, W.num_kv_heads, W.head_dim, W.page_tokens
+    T, SPLIT = 8192, 2048
+    width = 4 * T // PT
+    npg = [-(-c // PT) for c in final]
+    bases = np.concatenate([[0], np.cumsum(npg)[:-1]]).astype(np.int64)
+    Ph = int(sum(npg))
+    table = np.full((W.batch, width), -1, dtype=np.int32)
+    for b, n in enumerate(npg):
+        table[b, :n] = bases[b] + np.arange(n)        # each history contiguous per layer
+    plb = W.page_layer_bytes
+    resident = torch.zeros(Ph * plb * L // 2, dtype=torch.int16, device=dev)
+    new_k, new_v = {}, {}
+    qs = []
+    for layer in range(L):
+        qs.append(I.device_q(W, layer, dev))
+        for b in range(W.batch):
+            k, v = I.device_kv(W, layer, b, dev)
+            I.device_scatter(resident, W, layer, b, table[b], k, v)
+            new_k[layer, b] = k[:, sc["start"][b]:].contiguous()
+            new_v[layer, b] = v[:, sc["start"][b]:].contiguous()
+            del k, v
+    host = torch.empty(resident.numel(), dtype=torch.int16, pin_memory=True)
+    host.copy_(resident)
+    rpool = pkv.Pool(resident, L, Hkv)
+    dev_rtab = torch.tensor(table, dtype=torch.int32, device=dev)
+    arena = torch.zeros(sc["pool_pages"] * plb * L // 2, dtype=torch.int16, device=dev)
+    pool = pkv.Pool(arena, L, Hkv)
+    K_BUF = 2
+    sarena = torch.zeros(K_BUF * Ph * plb // 2, dtype=torch.int16, device=dev)
+    spool = pkv.Pool(sarena, K_BUF, Hkv)
+    copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    live = pkv.Live(pool, spool, host, W.batch, width, copy_s, compute, wb_s)
+    for c, (t, bu) in sc["contexts"].items():
+        live.add(c, t, bu)
+    S = 4
+    nbw = pkv.decode_workspace_bytes(W.batch, Hq, S * T, T, D, 0, SPLIT)
+    ws = torch.zeros(max(16, nbw) // 4 + 4, device=dev)
+    ws_r = torch.zeros_like(ws)
+    po = torch.empty((L, W.batch, Hq, S, D), device=dev)
+    pl = torch.empty((L, W.batch, Hq, S), device=dev)
+    outs = torch.empty((L, W.batch, Hq, D), device=dev)
+    lses = torch.empty((L, W.batch, Hq), device=dev)
+    rpo, rpl, routs, rlses = (torch.empty_like(x) for x in (po, pl, outs, lses))
+    length = list(sc["start"])
+
+    def live_step(ids, lens):
+        n = len(ids)
+        status, info = live.begin(ids, lens, table[ids])
+        for layer in range(L):
+            kn = torch.stack([new_k[layer, c][:, lens[i] - 1 - sc["start"][c]]
+                              for i, c in enumerate(ids)])
+            vn = torch.stack([new_v[layer, c][:, lens[i] - 1 - sc["start"][c]]
+                              for i, c in enumerate(ids)])
+            live.layer(layer, qs[layer][:n], kn, vn, T, W.scale, po[layer, :n], pl[layer, :n],
+                       outs[layer, :n], lses[layer, :n], workspace=ws, split_tokens=SPLIT)
+        return status, info
+
+    def resident_step(ids, lens):
+        n = len(ids)
+        dl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        rows = dev_rtab[ids].contiguous()
+        for layer in range(L):
+            pkv.decode_attention_merged(rpool, layer, qs[layer][:n], rows, dl, S * T, T, W.scale,
+                                        rpo[layer, :n], rpl[layer, :n], routs[layer, :n],
+                                        rlses[layer, :n], workspace=ws_r, split_tokens=SPLIT)
+
+    def same(a, b):
+        return bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+    # the schedule, every step and layer against the resident decode
+    ok = True
+    kinds = {}
+    for st in sc["steps"]:
+        for c, (t, bu) in st["set_target"].items():
+            live.set_target(c, t, bu)
+        ids, lens = st["ids"], st["lengths"]
+        for c, ln in zip(ids, lens):
+            length[c] = ln
+        live_step(ids, lens)
+        resident_step(ids, lens)
+        torch.cuda.synchronize()
+        n = len(ids)
+        ok = ok and all(same(x[:, :n], y[:, :n]) for x, y in
+                        ((po, rpo), (pl, rpl), (outs, routs), (lses, rlses)))
+        for e in live.admission.events():
+            kinds[e["kind"]] = kinds.get(e["kind"], 0) + 1
+    # steady steps: all four growing
+    ids = [0, 1, 2, 3]
+    infos = []
+
+    def grow_step():
+        for c in ids:
+            length[c] += 1
+        infos.append(live_step(ids, [length[c] for c in ids])[1])
+    for _ in range(args.warmup):
+        grow_step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    first = len(infos)
+    lens_timed = []
+    e0.record(compute)
+    for _ in range(args.steps):
+        grow_step()
+        lens_timed.append([length[c] for c in ids])
+    # the step ends when its last write-back has landed
+    done = torch.cuda.Event()
+    done.record(wb_s)
+    compute.wait_event(done)
+    e1.record(compute)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    timed = infos[first:]
+    # the resident decode of the same histories, same tiling
+    e0.record(compute)
+    for lens in lens_timed:
+        resident_step(ids, lens)
+    e1.record(compute)
+    torch.cuda.synchronize()
+    ms_res = e0.elapsed_time(e1) / args.steps
+    live.destroy()
+    staged = float(np.mean([i["staged_pages"] for i in timed]))
+    hot = float(np.mean([i["copied_in_pages"] for i in timed]))
+    kv = float(np.mean([sum(x) for x in lens_timed])) * 4096 * L
+    h2d = (staged + hot) * plb * L + W.batch * (width + 2) * 4
+    d2h = W.batch * L * 2 * Hkv * D * 2
+    hbm = kv + (staged + hot) * plb * L + d2h
+    return {
+        "metric": "decode attention KV GB/s (% of HBM peak) and tokens/s at 262K ctx, 1 GPU",
+        "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "live pool: 4 requests of ~31,744 tokens growing by one token per "
+                               "step, 16 layers, histories in pinned host memory (contiguous per "
+                               "layer), device pool of 1,491 pages (3/4 of the histories' pages), "
+                               "tile 8192 / split 2048, 2 staging buffers",
+                   "pool_pages": sc["pool_pages"], "history_pages": Ph},
+        "tokens_per_s": round(W.batch / (ms * 1e-3), 2),
+        "schedule_equals_resident_bitwise": ok,
+        "schedule_page_sources": kinds,
+        "per_step": {"staged_pages_per_layer": staged, "copied_in_pages": hot,
+                     "host_to_device_bytes": int(h2d), "device_to_host_bytes": int(d2h),
+                     "hbm_bytes": int(hbm), "kv_bytes_read": int(kv)},
+        "host_to_device_GBs": round(h2d / (ms * 1e-3) / 1e9, 2),
+        "resident_same_histories": {"ms_per_step": round(ms_res, 3),
+                                    "tokens_per_s": round(W.batch / (ms_res * 1e-3), 1),
+                                    "value": round(kv / (ms_res * 1e-3) / 1e9, 1)},
     }
 
 

@@ -177,13 +177,26 @@ int pkv_compact_crc(const pkv_pool* compact, const int32_t* dev_pages, int32_t n
  *   - no physical page appears twice in the whole table.
  * pkv_page_table_validate only checks.  pkv_page_table_write checks, then
  * copies both host arrays to the caller's device arrays on `stream` and
- * waits for that copy, so the host arrays may be reused on return (a table
- * changes between decode steps, not inside one). */
+ * waits for the stream to reach the end of that copy (so also for all work
+ * queued on it before), so the host arrays may be any host memory and may be
+ * reused on return: a set-up call.
+ * pkv_page_table_write_async is the per-step form (the host never waits on
+ * the step path: Staging without a stall, "Two copy queues and device-side
+ * ordering"): it checks, queues both copies on `stream` in stream order
+ * (after the decodes queued before it, which may still read dev_table) and,
+ * if done_event (a hipEvent_t) is not NULL, records it after them; it
+ * returns without waiting.  host_table and host_ctx_lens must be pinned host
+ * memory (hipHostMalloc) that the caller leaves unchanged until done_event
+ * has completed (e.g. a ring of such buffers, one per step in flight). */
 int pkv_page_table_validate(const pkv_pool* pool, const int32_t* host_table,
                             const int32_t* host_ctx_lens, int32_t batch, int32_t pt_stride);
 int pkv_page_table_write(const pkv_pool* pool, const int32_t* host_table,
                          const int32_t* host_ctx_lens, int32_t batch, int32_t pt_stride,
                          int32_t* dev_table, int32_t* dev_ctx_lens, void* stream);
+int pkv_page_table_write_async(const pkv_pool* pool, const int32_t* host_table,
+                               const int32_t* host_ctx_lens, int32_t batch, int32_t pt_stride,
+                               int32_t* dev_table, int32_t* dev_ctx_lens, void* stream,
+                               void* done_event);
 
 /* -------------------------------------------------------------- decode --
  * Per-tile partials of decode attention for one layer.

@@ -295,6 +295,26 @@ PKV_API int pkv_page_table_write(const pkv_pool* pool, const int32_t* host_table
   return ok();
 }
 
+PKV_API int pkv_page_table_write_async(const pkv_pool* pool, const int32_t* host_table,
+                                       const int32_t* host_ctx_lens, int32_t batch,
+                                       int32_t pt_stride, int32_t* dev_table,
+                                       int32_t* dev_ctx_lens, void* stream, void* done_event) {
+  if (int rc = pkv_page_table_validate(pool, host_table, host_ctx_lens, batch, pt_stride))
+    return rc;
+  if (batch == 0) return ok();
+  if (!dev_table || !dev_ctx_lens) return fail(PKV_ERR_INVALID_ARG, "dev_table or dev_ctx_lens is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dev_table, host_table, sizeof(int32_t) * (size_t)batch * pt_stride,
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dev_ctx_lens, host_ctx_lens, sizeof(int32_t) * (size_t)batch,
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && done_event) e = hipEventRecord(static_cast<hipEvent_t>(done_event), s);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_DEVICE, "page-table copy failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 PKV_API int pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                        int32_t token_count, int32_t tile_tokens,
                                        const pkv_decode_opts* opts, uint64_t* bytes_out) {

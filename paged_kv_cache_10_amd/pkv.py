@@ -34,6 +34,7 @@ EXPORTS = [
     "pkv_compact_convert", "pkv_compact_crc", "pkv_plan_tiles", "pkv_decode_attention_rows",
     "pkv_decode_attention_merged", "pkv_decode_attention_runs",
     "pkv_decode_attention_merged_noalloc",
+    "pkv_page_table_write_async",
     "pkv_live_create", "pkv_live_add", "pkv_live_set_target", "pkv_live_remove",
     "pkv_live_admission", "pkv_live_step_begin", "pkv_live_layer", "pkv_live_destroy",
 ]
@@ -117,6 +118,7 @@ def lib():
         L.pkv_compact_crc.argtypes = [P, P, I32, P, P]
         L.pkv_page_table_validate.argtypes = [P, I32P, I32P, I32, I32]
         L.pkv_page_table_write.argtypes = [P, I32P, I32P, I32, I32, P, P, P]
+        L.pkv_page_table_write_async.argtypes = [P, P, P, I32, I32, P, P, P, P]
         L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32,
                                                  ctypes.POINTER(DecodeOpts), ctypes.POINTER(U64)]
         L.pkv_decode_attention.argtypes = [P, I32, P, P, I32, P, I32, I32, I32, I32, I32,
@@ -277,6 +279,33 @@ def page_table_write(pool, table, ctx_lens, dev_table, dev_ctx_lens, stream=None
                                       _ptr(dev_table, torch.int32, "dev_table"),
                                       _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"),
                                       _stream(stream)))
+
+
+def page_table_write_async(pool, host_table, host_ctx_lens, dev_table, dev_ctx_lens,
+                           stream=None, done_event=None):
+    """Validate pinned host tensors (int32 [batch, pt_stride] and [batch])
+    and queue their copy into the device tensors on `stream` without
+    waiting; records done_event (a torch.cuda.Event) after the copy.  The
+    host tensors must stay unchanged until done_event completes."""
+    import torch
+    if not (host_table.is_pinned() and host_ctx_lens.is_pinned()):
+        raise ValueError("host_table and host_ctx_lens must be pinned host tensors")
+    if host_table.dtype != torch.int32 or host_ctx_lens.dtype != torch.int32:
+        raise ValueError("host_table and host_ctx_lens must be int32")
+    if host_table.dim() != 2 or not host_table.is_contiguous() or \
+            tuple(host_ctx_lens.shape) != (host_table.shape[0],):
+        raise ValueError("host_table must be a contiguous [batch, pt_stride], ctx_lens [batch]")
+    if dev_table.numel() < host_table.numel() or dev_ctx_lens.numel() < host_ctx_lens.numel():
+        raise ValueError("device table / ctx_lens tensors are too small")
+    ev = None
+    if done_event is not None:
+        if done_event.cuda_event == 0:          # torch creates the event on its first record
+            done_event.record(torch.cuda.current_stream() if stream is None else stream)
+        ev = done_event.cuda_event
+    _check(lib().pkv_page_table_write_async(
+        pool.handle, host_table.data_ptr(), host_ctx_lens.data_ptr(), host_table.shape[0],
+        host_table.shape[1], _ptr(dev_table, torch.int32, "dev_table"),
+        _ptr(dev_ctx_lens, torch.int32, "dev_ctx_lens"), _stream(stream), ev))
 
 
 def decode_workspace_bytes(batch, num_q_heads, token_count, tile_tokens, head_dim=256,

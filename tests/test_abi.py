@@ -184,6 +184,21 @@ def test_decode_arguments_are_refused_on_the_host(kw, code, needle):
     assert rc == code and needle in msg, msg
 
 
+def test_async_table_write_validates_before_queueing():
+    """The asynchronous table write refuses a bad row on the host, with the
+    same checks as the synchronous one, before any copy is queued."""
+    import numpy as np
+    L = pkv.lib()
+    pool = FakePool(64)
+    t = np.array([[3, 3, -1, -1]], dtype=np.int32)          # a page twice
+    c = np.array([100], dtype=np.int32)
+    rc = L.pkv_page_table_write_async(pool.handle, t.ctypes.data, c.ctypes.data, 1, 4,
+                                      1 << 20, 1 << 21, None, None)
+    assert rc == -5 and "twice" in err()
+    assert L.pkv_page_table_write_async(pool.handle, None, None, 0, 4, None, None, None,
+                                        None) == 0             # no rows: nothing to copy
+
+
 def test_noalloc_decode_refuses_more_than_its_static_scratch():
     """pkv_decode_attention_merged_noalloc refuses, on the host and before
     touching any device, a call whose split partials exceed the library's
