@@ -38,9 +38,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
 # Valid only for the kernel source it was measured on.
 PMC_TRAFFIC = {
-    "source_sha256": "b04ff7e6ad37e97da8cbc69fbc98181856bc276c36435816aeacf2bbe0a856ae",
+    "source_sha256": "0fa0ab04f3cd7fddb50f0e1acbdbd636d5ff8f963f8579608aeaa6c77e15c9c1",
     "workload": "long262k", "tile": 4096, "split": 4096,
-    "fetch_kib": 524499.8, "fetch_scale": 1048576 / 524300.1,
+    "fetch_kib": 524503.3, "fetch_scale": 1048576 / 524300.1,
     "write_kib": 1584.0, "write_scale": 1.0,
 }
 KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_10_amd/csrc/decode_exact.h",
@@ -50,9 +50,9 @@ KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_
 # decode kernel plus the tile finalize launch, FETCH_SIZE and WRITE_SIZE of
 # both dispatches added, calibrated on the plain copy of the same runs.
 PMC_TRAFFIC_CONC = {
-    "source_sha256": "a4f14d4c7a2e39100d5b7e488bbad82c4ff6d887b461ca1939ba595d538164e5",
+    "source_sha256": "c8042e0d6d5ac821c6861c2fb06930c779770f0a735ca6b9d6b90eda4cbe1522",
     "workload": "conc", "tile": 8192, "split": 2048,
-    "fetch_kib": 254290.4 + 845.0, "fetch_scale": 1048576 / 524300.4,
+    "fetch_kib": 254293.9 + 845.0, "fetch_scale": 1048576 / 524300.1,
     "write_kib": 1584.4 + 387.0, "write_scale": 1.0,
 }
 CONC_SOURCES = KERNEL_SOURCES + ("paged_kv_cache_10_amd/csrc/merge.hip",)
@@ -62,8 +62,8 @@ CONC_SOURCES = KERNEL_SOURCES + ("paged_kv_cache_10_amd/csrc/merge.hip",)
 PMC_TRAFFIC_MIXED = {
     "source_sha256": PMC_TRAFFIC["source_sha256"],
     "workload": "mixed", "plan": 256,
-    "fetch_kib": 854222.6, "fetch_scale": 1048576 / 524301.1,
-    "write_kib": 5922.3, "write_scale": 1.0,
+    "fetch_kib": 854230.6, "fetch_scale": 1048576 / 524301.2,
+    "write_kib": 5922.5, "write_scale": 1.0,
 }
 
 # The same for the compact kernel on the 262K compact-older workload
@@ -87,6 +87,16 @@ PMC_TRAFFIC_RUNS = {
 RUNS_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_runs.hip", "paged_kv_cache_10_amd/csrc/decode_compact.h",
                 "paged_kv_cache_10_amd/csrc/decode_exact.h", "paged_kv_cache_10_amd/csrc/compact.h",
                 "paged_kv_cache_10_amd/csrc/device.h")
+
+
+# The same for the merge alone on the merge-stress shape (merge_kernel, 64 x
+# 24 rows x 256 partials), calibrated on the plain copy of the same runs.
+PMC_TRAFFIC_MERGE = {
+    "source_sha256": "ff2d2306ca2f6e7fa835fb38468f931fd63e4b95dab8a1803f0a8109d471ea22",
+    "fetch_kib": 197466.5, "fetch_scale": 1048576 / 524301.2,
+    "write_kib": 1584.0, "write_scale": 1.0,
+}
+MERGE_SOURCES = ("paged_kv_cache_10_amd/csrc/merge.hip", "paged_kv_cache_10_amd/csrc/device.h")
 
 
 def sources_sha256(files):
@@ -236,6 +246,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also capture the timed step in a HIP graph and time its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the 4-request, mixed and merge-stress lines the default run adds")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -531,6 +543,14 @@ def main():
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, qs, args.cpu_seconds)
+
+    default_run = (args.workload == "long262k" and not (args.tile or args.staged or args.separate
+                                                        or args.overlap or args.graph
+                                                        or args.kernel != "mfma"))
+    if default_run and not args.no_others:
+        del arena, pool, po, pl, outs, lses, qs
+        torch.cuda.empty_cache()
+        res["other_workloads"] = other_workloads(args)
 
     print(json.dumps(res), flush=True)
     return 0
@@ -876,11 +896,52 @@ def merge_stress(args, ceiling):
         "roofline": {"bound": "hbm", "kernel": "merge_kernel", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5),
-                     "traffic": None},
+                     "traffic": merge_traffic()},
     }
     if ceiling is not None:
         res["read_ceiling"] = ceiling
+    if args.copy_probe:
+        res["copy_probe"] = copy_probe(dev, stream)
     return res
+
+
+def merge_traffic():
+    """Counter-derived HBM bytes of one merge-stress call, or None if they
+    were not taken on this merge source."""
+    t = PMC_TRAFFIC_MERGE
+    if t["source_sha256"] is None or sources_sha256(MERGE_SOURCES) != t["source_sha256"]:
+        return None
+    return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+
+
+def other_workloads(args):
+    """The 4-request, mixed and merge-stress workloads, each measured by a
+    child run of this script (its own process and device memory) with the
+    same step counts: the key figures of each line."""
+    import subprocess
+    here = os.path.abspath(__file__)
+    runs = {"conc": ["--workload", "conc"], "mixed": ["--workload", "mixed"],
+            "merge_stress": ["--merge-stress"]}
+    out = {}
+    for name, extra in runs.items():
+        cmd = [sys.executable, here, "--no-cpu-baseline", "--no-read-probe", "--no-others",
+               "--steps", str(args.steps), "--warmup", str(args.warmup)] + extra
+        p = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
+        if p.returncode != 0 or not lines:
+            out[name] = {"error": f"exit {p.returncode}: {p.stderr.strip()[-300:]}"}
+            continue
+        d = json.loads(lines[-1])
+        r = d["roofline"]
+        out[name] = {"workload": d["config"]["workload"], "ms_per_step": d["ms_per_step"],
+                     "value": d["value"], "unit": d["unit"],
+                     "hbm_frac": round(d["value"] / HBM_PEAK_GBS, 4),
+                     **({"tokens_per_s": d["tokens_per_s"]} if "tokens_per_s" in d else {}),
+                     "roofline": {k: r.get(k) for k in ("kernel", "achieved", "frac",
+                                                        "avg_launch_ms",
+                                                        "algorithmic_bytes_per_launch",
+                                                        "traffic")}}
+    return out
 
 
 def total_bytes_step(w, slots, split_slots=0):
