@@ -586,7 +586,9 @@ int pkv_admit_destroy(pkv_admit* a);
  *               the step's composed table, lengths and append positions.
  *   streams     copy (host -> device pages), compute (table copy, append,
  *               decode, merge) and write-back (new rows -> host), the
- *               caller's, default priority.
+ *               caller's, default priority.  Every run of pages is copied as
+ *               two halves, one on the copy stream and one on a second copy
+ *               stream the runtime creates and owns (default priority).
  *   The runtime allocates a pinned ring of 4 step tables (host memory, at
  *   create) and never device memory.
  * pkv_live_add / pkv_live_set_target / pkv_live_remove: contexts, with the

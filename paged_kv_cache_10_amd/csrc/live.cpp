@@ -16,7 +16,9 @@
 // a small pinned ring, on the compute stream.
 //
 // Per layer, on the device, ordered by events only:
-//   copy stream      waits for the previous step's write-back of this layer
+//   copy streams     (the caller's and the runtime's own second one, each
+//                    taking half of every run of pages) wait for the
+//                    previous step's write-back of this layer
 //                    (its pool pages and host rows are then settled) and for
 //                    the last layer that read this staging buffer; copies in
 //                    the hot pages' slices of this layer and the staged pages
@@ -70,7 +72,8 @@ struct pkv_live {
   hipEvent_t ring_ev[kRing] = {};
   bool ring_used[kRing] = {};
   hipStream_t copy = nullptr, compute = nullptr, writeback = nullptr;
-  hipEvent_t copied = nullptr, consumed = nullptr;
+  hipStream_t copy2 = nullptr;          // the runtime's own second copy stream
+  hipEvent_t copied = nullptr, copied2 = nullptr, consumed = nullptr;
   std::vector<hipEvent_t> layer_done;   // after the write-back of layer l
   std::vector<char> layer_done_set;
   std::vector<hipEvent_t> buf_done;     // after the write-back of the last layer using buffer k
@@ -97,9 +100,11 @@ int quarantine(pkv_live* L, hipError_t e, const char* what) {
 }
 
 // Copies of whole (layer, page) slices; runs of consecutive destination and
-// host pages go as one copy.
+// host pages go as one copy, its first half on s0 and the rest on s1 (two
+// copy engines, so that one's wait before a layer overlaps the other's
+// transfer).
 hipError_t copy_pages(const std::vector<PageCopy>& pages, char* dst_slab, const char* host_slab,
-                      uint64_t plb, hipStream_t s) {
+                      uint64_t plb, hipStream_t s0, hipStream_t s1) {
   size_t i = 0;
   hipError_t e = hipSuccess;
   while (i < pages.size() && e == hipSuccess) {
@@ -107,9 +112,14 @@ hipError_t copy_pages(const std::vector<PageCopy>& pages, char* dst_slab, const 
     while (i + run < pages.size() && pages[i + run].dst == pages[i].dst + (int32_t)run &&
            pages[i + run].host == pages[i].host + (int32_t)run)
       ++run;
+    const size_t half = (run + 1) / 2;
     e = hipMemcpyAsync(dst_slab + (uint64_t)pages[i].dst * plb,
-                       host_slab + (uint64_t)pages[i].host * plb, run * plb,
-                       hipMemcpyHostToDevice, s);
+                       host_slab + (uint64_t)pages[i].host * plb, half * plb,
+                       hipMemcpyHostToDevice, s0);
+    if (e == hipSuccess && run > half)
+      e = hipMemcpyAsync(dst_slab + (uint64_t)(pages[i].dst + (int32_t)half) * plb,
+                         host_slab + (uint64_t)(pages[i].host + (int32_t)half) * plb,
+                         (run - half) * plb, hipMemcpyHostToDevice, s1);
     i += run;
   }
   return e;
@@ -118,6 +128,7 @@ hipError_t copy_pages(const std::vector<PageCopy>& pages, char* dst_slab, const 
 void destroy_events(pkv_live* L) {
   for (auto& ev : L->ring_ev) if (ev) (void)hipEventDestroy(ev);
   if (L->copied) (void)hipEventDestroy(L->copied);
+  if (L->copied2) (void)hipEventDestroy(L->copied2);
   if (L->consumed) (void)hipEventDestroy(L->consumed);
   for (auto ev : L->layer_done) if (ev) (void)hipEventDestroy(ev);
   for (auto ev : L->buf_done) if (ev) (void)hipEventDestroy(ev);
@@ -183,6 +194,8 @@ PKV_API int pkv_live_create(const pkv_pool* pool, const pkv_pool* stage, void* h
   for (auto& ev : L->ring_ev)
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&L->copied, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&L->copied2, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&L->copy2, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&L->consumed, hipEventDisableTiming);
   for (auto& ev : L->layer_done)
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
@@ -190,6 +203,7 @@ PKV_API int pkv_live_create(const pkv_pool* pool, const pkv_pool* stage, void* h
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   if (e != hipSuccess) {
     destroy_events(L);
+    if (L->copy2) (void)hipStreamDestroy(L->copy2);
     if (L->ring) (void)hipHostFree(L->ring);
     pkv_admit_destroy(L->admit);
     delete L;
@@ -378,16 +392,21 @@ PKV_API int pkv_live_layer(pkv_live* L, int32_t layer, const void* q, const void
   const uint64_t plb = L->pool->page_layer_bytes;
   // 1. copies of this layer's hot and staged pages, after their last readers
   hipError_t e = hipSuccess;
-  if (L->layer_done_set[(size_t)layer]) e = hipStreamWaitEvent(L->copy, L->layer_done[(size_t)layer], 0);
-  if (e == hipSuccess && L->buf_done_set[(size_t)buf])
-    e = hipStreamWaitEvent(L->copy, L->buf_done[(size_t)buf], 0);
+  for (hipStream_t cs : {L->copy, L->copy2}) {
+    if (e == hipSuccess && L->layer_done_set[(size_t)layer])
+      e = hipStreamWaitEvent(cs, L->layer_done[(size_t)layer], 0);
+    if (e == hipSuccess && L->buf_done_set[(size_t)buf])
+      e = hipStreamWaitEvent(cs, L->buf_done[(size_t)buf], 0);
+  }
   const char* hslab = L->host + (uint64_t)layer * (uint64_t)L->host_pages * plb;
   char* pslab = static_cast<char*>(L->pool->base) + (uint64_t)layer * (uint64_t)L->pool->num_pages * plb;
   char* sslab = static_cast<char*>(L->stage->base) + (uint64_t)buf * (uint64_t)L->stage->num_pages * plb;
-  if (e == hipSuccess) e = copy_pages(L->hot, pslab, hslab, plb, L->copy);
-  if (e == hipSuccess) e = copy_pages(L->staged, sslab, hslab, plb, L->copy);
+  if (e == hipSuccess) e = copy_pages(L->hot, pslab, hslab, plb, L->copy, L->copy2);
+  if (e == hipSuccess) e = copy_pages(L->staged, sslab, hslab, plb, L->copy, L->copy2);
   if (e == hipSuccess) e = hipEventRecord(L->copied, L->copy);
+  if (e == hipSuccess) e = hipEventRecord(L->copied2, L->copy2);
   if (e == hipSuccess) e = hipStreamWaitEvent(L->compute, L->copied, 0);
+  if (e == hipSuccess) e = hipStreamWaitEvent(L->compute, L->copied2, 0);
   if (e != hipSuccess) return quarantine(L, e, "layer copies");
   // 2. append the new token, decode over the composed table, merge
   int rc = pkv_append_kv(L->pool, layer, dev_table, L->pt_stride, dev_pos, L->n, k_new, v_new,
@@ -436,9 +455,11 @@ PKV_API int pkv_live_destroy(pkv_live* L) {
   if (!L) return PKV_OK;
   // the streams may still read the ring and the host rows: wait for them
   (void)hipStreamSynchronize(L->copy);
+  (void)hipStreamSynchronize(L->copy2);
   (void)hipStreamSynchronize(L->compute);
   (void)hipStreamSynchronize(L->writeback);
   destroy_events(L);
+  (void)hipStreamDestroy(L->copy2);
   if (L->ring) (void)hipHostFree(L->ring);
   pkv_admit_destroy(L->admit);
   delete L;
