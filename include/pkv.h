@@ -600,8 +600,11 @@ int pkv_admit_destroy(pkv_admit* a);
  *   _PARTIAL, _REFUSED_STEP; a refused context decodes nothing, out 0 and
  *   lse -inf, and is not appended) and *info (may be NULL).  Runs admission,
  *   composes the table and queues its copy on the compute stream; waits on
- *   the host only when the ring is full (the GPU 4 steps behind).  Refused
- *   with PKV_ERR_LEASE while the previous step has a layer not yet run.
+ *   the host only when the ring is full (the GPU 4 steps behind).  A step
+ *   is open from its begin until its last layer is queued: meanwhile a new
+ *   begin and pkv_live_remove are refused with PKV_ERR_LEASE.  A context
+ *   removed and added again under the same id takes none of its old pages'
+ *   bytes (its pages are copied in afresh).
  * pkv_live_layer: one layer of the open step, each layer once.  On the copy
  *   stream, after the previous step's write-back of this layer and the last
  *   reader of the staging buffer: the hot pages' and staged pages' slices

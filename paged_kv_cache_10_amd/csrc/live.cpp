@@ -229,7 +229,7 @@ PKV_API int pkv_live_set_target(pkv_live* L, int32_t ctx, int32_t target_pages,
 
 PKV_API int pkv_live_remove(pkv_live* L, int32_t ctx) {
   if (!L) return fail(PKV_ERR_INVALID_ARG, "live pool is NULL");
-  if (L->open) return fail(PKV_ERR_LEASE, "a step is open: run its layers before removing");
+  if (L->open) return fail(PKV_ERR_LEASE, "a step is open: run its layers before removing a context");
   const int rc = pkv_admit_remove(L->admit, ctx);
   if (rc != PKV_OK) return rc;
   // its pages keep their bytes, but no later context of the same id may
@@ -251,7 +251,7 @@ PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
                                 int32_t host_stride, int32_t* status, pkv_live_info* info) {
   if (!L) return fail(PKV_ERR_INVALID_ARG, "live pool is NULL");
   if (L->quarantined) return fail(PKV_ERR_QUARANTINED, "live pool is quarantined; destroy it");
-  if (L->open && L->layers_run < L->layers)
+  if (L->open)
     return pkv::set_error(PKV_ERR_LEASE, "step %llu has run %d of %d layers; every layer runs "
                           "once per step before the next step begins",
                           (unsigned long long)L->steps, L->layers_run, L->layers);
@@ -446,7 +446,7 @@ PKV_API int pkv_live_layer(pkv_live* L, int32_t layer, const void* q, const void
   L->layer_done_set[(size_t)layer] = 1;
   L->buf_done_set[(size_t)buf] = 1;
   L->layer_run[(size_t)layer] = 1;
-  ++L->layers_run;
+  if (++L->layers_run == L->layers) L->open = false;     // every layer queued: the step is done
   pkv::clear_error();
   return PKV_OK;
 }

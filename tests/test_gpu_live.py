@@ -137,3 +137,135 @@ def test_live_pool_steps_equal_resident_and_oracle(gpu):
             I.device_scatter(expect, W, layer, b, table[b], k, v, pad_value=NAN16)
     assert torch.equal(host.to(DEV), expect)
     live.destroy()
+
+
+def test_live_pool_refusal_readmission_and_reused_ids(gpu):
+    """A 12-page pool for four contexts: D is refused (no sink to be had)
+    for four steps, then admitted by evicting C while C pauses; C is then
+    refused.  A refused context's row is (0, -inf) and its token is not
+    appended (the caller retries it).  A is removed and re-added under the
+    same id with another history: no page may keep serving A's old bytes.
+    Every served row is bitwise equal to a resident decode and matches the
+    oracle; the host copy ends with exactly the tokens that were served."""
+    L, Hq, Hkv, D, T = 2, 24, 4, 256, 1024
+    start = {"A": 700, "B": 1500, "C": 300, "D": 200, "A2": 900}
+    grow = 13
+    hist = {h: I.Workload(f"live-{h}", seed=200 + i, ctx_lens=[n + grow], num_layers=L,
+                          tile_tokens=T) for i, (h, n) in enumerate(start.items())}
+    npg = {h: -(-w.ctx_lens[0] // 64) for h, w in hist.items()}
+    base, o = {}, 0
+    for h in start:
+        base[h] = o
+        o += npg[h]
+    Ph, width = o, 32
+    plb = hist["A"].page_layer_bytes
+    rows = {h: np.full(width, -1, np.int32) for h in start}
+    for h in start:
+        rows[h][:npg[h]] = base[h] + np.arange(npg[h])
+    resident = torch.full((Ph * plb * L // 2,), NAN16, dtype=torch.int16, device=DEV)
+    first = torch.full_like(resident, NAN16)
+    kv = {}
+    for h, w in hist.items():
+        for layer in range(L):
+            k, v = I.device_kv(w, layer, 0, DEV)
+            kv[h, layer] = (k, v)
+            I.device_scatter(resident, w, layer, 0, rows[h], k, v, pad_value=NAN16)
+            s0 = start[h]
+            I.device_scatter(first, w, layer, 0, rows[h], k[:, :s0], v[:, :s0], pad_value=NAN16)
+    host = torch.empty(resident.numel(), dtype=torch.int16, pin_memory=True)
+    host.copy_(first)
+    rpool = pkv.Pool(resident, L, Hkv)
+    arena = torch.full((12 * plb * L // 2,), NAN16, dtype=torch.int16, device=DEV)
+    pool = pkv.Pool(arena, L, Hkv)
+    sarena = torch.full((2 * 64 * plb // 2,), NAN16, dtype=torch.int16, device=DEV)
+    spool = pkv.Pool(sarena, 2, Hkv)
+    copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
+    live = pkv.Live(pool, spool, host, 4, width, copy_s, torch.cuda.current_stream(), wb_s)
+    ctx_hist = {9: "B", 5: "A", 2: "C"}
+    live.add(9, 6, 0)
+    live.add(5, 4, 2)
+    live.add(2, 3, 0)
+    length = {h: start[h] for h in start}
+    refusals = 0
+    for s in range(1, 13):
+        if s == 4:
+            live.add(7, 3, 0)
+            ctx_hist[7] = "D"
+        if s == 7:
+            live.remove(5)
+            live.add(5, 4, 0)
+            ctx_hist[5] = "A2"
+        ids = [9, 5] + ([2] if s != 8 else []) + ([7] if s >= 4 else [])
+        hs = [ctx_hist[c] for c in ids]
+        lens = [length[h] + 1 for h in hs]
+        n = len(ids)
+        status, info = live.begin(ids, lens, np.stack([rows[h] for h in hs]))
+        S = 2
+        for layer in range(L):
+            q = step_q(300, s, layer, 4)[:n].contiguous()
+            kn = torch.stack([kv[h, layer][0][:, ln - 1] for h, ln in zip(hs, lens)]).contiguous()
+            vn = torch.stack([kv[h, layer][1][:, ln - 1] for h, ln in zip(hs, lens)]).contiguous()
+            got = [torch.full((n, Hq, S, D), float("nan"), device=DEV),
+                   torch.full((n, Hq, S), float("nan"), device=DEV),
+                   torch.full((n, Hq, D), float("nan"), device=DEV),
+                   torch.full((n, Hq), float("nan"), device=DEV)]
+            live.layer(layer, q, kn, vn, T, 1 / 16, *got)
+            ref = [torch.full_like(x, float("nan")) for x in got]
+            rlens = [0 if st == "refused" else ln for st, ln in zip(status, lens)]
+            rrows = torch.tensor(np.stack([rows[h] for h in hs]), dtype=torch.int32, device=DEV)
+            pkv.decode_attention_merged(rpool, layer, q, rrows,
+                                        torch.tensor(rlens, dtype=torch.int32, device=DEV),
+                                        S * T, T, 1 / 16, *ref)
+            torch.cuda.synchronize()
+            for x, y in zip(got, ref):
+                assert same_bits(x, y), (s, layer)
+            qf = oracle.widen_bf16(q.view(torch.int16).cpu().numpy().view(np.uint16))
+            for i, (h, st) in enumerate(zip(hs, status)):
+                if st == "refused":
+                    assert (got[2][i] == 0).all() and (got[3][i] == float("-inf")).all()
+                    continue
+                k, v = kv[h, layer]
+                kf = oracle.widen_bf16(k.view(torch.int16).cpu().numpy().view(np.uint16))
+                vf = oracle.widen_bf16(v.view(torch.int16).cpu().numpy().view(np.uint16))
+                eo, el = oracle.decode_one_pass(qf[i], kf, vf, lens[i], 1 / 16, Hkv)
+                assert_out_close(got[2][i].cpu().numpy(), eo, what=f"step {s} {h} out")
+                assert_lse_close(got[3][i].cpu().numpy(), el, what=f"step {s} {h} lse")
+        for h, ln, st in zip(hs, lens, status):
+            if st == "refused":
+                refusals += 1
+            else:
+                length[h] = ln
+        print(f"step {s}: {list(zip(ids, status))} {info}", flush=True)
+    torch.cuda.synchronize()
+    assert refusals >= 5 and length["D"] > start["D"] and length["A2"] > start["A2"]
+    expect = torch.full_like(resident, NAN16)
+    for h, w in hist.items():
+        for layer in range(L):
+            k, v = kv[h, layer]
+            n_ = length[h]
+            I.device_scatter(expect, w, layer, 0, rows[h], k[:, :n_], v[:, :n_], pad_value=NAN16)
+    assert torch.equal(host.to(DEV), expect)
+    live.destroy()
+
+
+def test_live_pool_refuses_a_step_that_overflows_its_staging_pool(gpu):
+    """A step that stages more pages than the staging pool holds is refused
+    with a message naming the setting, and the runtime is quarantined."""
+    L, Hkv = 2, 4
+    w = I.Workload("live-small", seed=401, ctx_lens=[2000], num_layers=L, tile_tokens=1024)
+    plb = w.page_layer_bytes
+    host = torch.zeros(32 * plb * L // 2, dtype=torch.int16, pin_memory=True)
+    arena = torch.zeros(4 * plb * L // 2, dtype=torch.int16, device=DEV)
+    sarena = torch.zeros(2 * 8 * plb // 2, dtype=torch.int16, device=DEV)
+    pool, spool = pkv.Pool(arena, L, Hkv), pkv.Pool(sarena, 2, Hkv)
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    live = pkv.Live(pool, spool, host, 1, 32, s0, torch.cuda.current_stream(), s1)
+    live.add(1, 4, 0)
+    row = np.arange(32, dtype=np.int32)[None]
+    with pytest.raises(pkv.PkvError) as e:
+        live.begin([1], [2000], row)                 # 32 pages, 4 resident: 28 to stage > 8
+    assert e.value.name == "PKV_ERR_PAGE_TABLE" and "staging pool" in str(e.value)
+    with pytest.raises(pkv.PkvError) as e:
+        live.begin([1], [2000], row)
+    assert e.value.name == "PKV_ERR_QUARANTINED"
+    live.destroy()
