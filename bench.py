@@ -69,7 +69,7 @@ PMC_TRAFFIC_MIXED = {
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "81e902467739c7a54d0883608d22293b7bc6a68415ab5abe8a33893c8ab7faeb",
+    "source_sha256": "0aaa68522b8ae01a6e34bf64e369341e7503ef6c59920b72e173a3a6910774b4",
     "workload": "long262k", "tile": 4800, "split": 4800,
     "fetch_kib": 230053.1, "fetch_scale": 1048576 / 524299.5,
     "write_kib": 1188.0, "write_scale": 1.0,
@@ -79,9 +79,9 @@ FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_a
 
 # The same for the one-launch kernel of both runs (COMPACT_LAUNCH, "one_launch").
 PMC_TRAFFIC_RUNS = {
-    "source_sha256": "750bf3dfc1a6c74e0e8b15432ee2377b07373bdb310bfc2373fcf1ebe4f2be1d",
+    "source_sha256": "d43d6b6559212bbce94ed3dbb077a15bbe475cb6ac01bd8edb8b0083fb6487bb",
     "workload": "long262k", "tile": 4800, "exact_tile": 2048,
-    "fetch_kib": 295727.6, "fetch_scale": 1048576 / 524299.5,
+    "fetch_kib": 295722.0, "fetch_scale": 1048576 / 524299.5,
     "write_kib": 1584.1, "write_scale": 1.0,
 }
 RUNS_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_runs.hip", "paged_kv_cache_10_amd/csrc/decode_compact.h",
