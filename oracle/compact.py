@@ -64,14 +64,21 @@ def e4m3_encode(y):
     sign is the input's sign bit (so -0.0 and negatives that round to zero
     give 0x80).
 
-    Saturation is a clamp to +-448 (exact; it keeps the sign of zero); the
-    rounding is torch's float8_e4m3fn conversion, a library routine for
-    exactly this round-to-nearest-even (pinned against the format's value
-    table by brute force in the tests)."""
-    import torch
+    Written out on the value table: the codes 0..126 hold the non-negative
+    finite values in increasing order, so |y| lies between the first value
+    at or above it (hi) and the one before (lo); the nearer of the two wins,
+    an equal distance goes to the code whose lowest bit is 0."""
     y = np.asarray(y, dtype=np.float32)
-    t = torch.from_numpy(np.ascontiguousarray(y)).clamp(-E4M3_MAX, E4M3_MAX)
-    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy().reshape(y.shape)
+    a = np.abs(y.astype(np.float64))                       # exact
+    hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_hi = _POS[hi] - a
+    d_lo = a - _POS[lo]
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(take_lo, lo, hi)
+    code = np.where(a >= E4M3_MAX, 126, code)             # saturate at 448
+    return (code.astype(np.uint8) | np.where(np.signbit(y), 0x80, 0).astype(np.uint8)).reshape(
+        y.shape)
 
 
 def e4m3_decode(codes):

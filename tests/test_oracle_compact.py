@@ -129,6 +129,17 @@ def pin_torch_decode(m):
     np.testing.assert_array_equal(m.decode(codes), ref)
 
 
+def pin_torch_encode(m):
+    """torch's float8_e4m3fn conversion rounds to nearest, ties to even; after
+    a clamp to +-448 (exact, keeps the sign of zero) it is the encoding."""
+    r = np.random.default_rng(11)
+    y = np.concatenate([r.standard_normal(20000) * 10.0 ** r.uniform(-5, 3, 20000),
+                        (C._POS[:-1] + C._POS[1:]) / 2.0, [0.0, -0.0, 448.0, -500.0]])
+    y = y.astype(np.float32)
+    t = torch.from_numpy(y).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(m.encode(y), t.view(torch.uint8).numpy())
+
+
 def brute_encode(y):
     """The definition by brute force over the value table: the nearest of
     the 127 non-negative finite values to |y| (ties to the even code), past
@@ -201,7 +212,7 @@ def pin_crc(m):
 
 
 PINS = [pin_golden_decode, pin_golden_encode, pin_golden_block, pin_torch_decode,
-        pin_brute_force_encode, pin_saturation, pin_round_trip, pin_block_properties, pin_crc]
+        pin_torch_encode, pin_brute_force_encode, pin_saturation, pin_round_trip, pin_block_properties, pin_crc]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
