@@ -286,3 +286,16 @@ def test_two_runs_splits_at_the_boundary():
     assert not np.array_equal(got[:128], x[:128])
     with pytest.raises(ValueError):
         C.two_runs(bits, 100)
+
+
+def test_block_scale_definition():
+    """block_scale: 1 for an all-zero block, else amax / 448 rounded once to
+    FP32 (amax of the magnitudes, the sign of the extreme value ignored)."""
+    assert C.block_scale(np.zeros((64, 256), np.float32)) == np.float32(1.0)
+    assert C.block_scale(np.array([[0.0, -448.0], [3.0, 1.0]], np.float32)) == np.float32(1.0)
+    s = C.block_scale(np.array([[-0.5, 0.25], [1.0, -2.0]], np.float32))
+    assert s.dtype == np.float32 and s == np.float32(2.0 / 448.0)
+    # 1 / 448 is not a binary fraction: the FP32 rounding of the exact quotient
+    exact = 1.0 / 448.0
+    s1 = C.block_scale(np.array([1.0], np.float32))
+    assert abs(float(s1) - exact) <= abs(float(np.nextafter(s1, np.float32(1))) - float(s1)) / 2
