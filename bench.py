@@ -230,6 +230,9 @@ def parse():
                     help="merge on the decode stream (the default)")
     ap.add_argument("--overlap", action="store_true",
                     help="merge layer l on a second stream while layer l+1 decodes")
+    ap.add_argument("--window-streams", type=int, default=2,
+                    help="--staged: streams the windows of a layer are spread over (they write "
+                         "disjoint slots and run concurrently; 1 = one after the other)")
     ap.add_argument("--host-staged", action="store_true",
                     help="history in pinned host memory, staged per 32K window under leases")
     ap.add_argument("--compact-older", action="store_true",
@@ -288,8 +291,14 @@ def main():
     # a 32,768-token window decoded alone holds 1/8 of the history: 512-token
     # splits give its launch 256 work-groups (4,096-token ones only 32), and
     # 512-token tiles (64 partials per head per window) need no tile finalize
-    w.tile_tokens = args.tile or (512 if args.staged else launch.get("tile", w.tile_tokens))
-    args.split = args.split or (512 if args.staged else launch.get("split", 0))
+    # staged windows spread over two streams run two at a time: 1,024-token
+    # tiles give each window 128 work-groups, two windows fill the GPU; one
+    # window at a time needs 512-token tiles to fill it alone (measured at
+    # 262K: 3.27 ms per step against 3.72 one window at a time; 2,048-token
+    # tiles on 4 streams 3.33, 1,024 on 3 or 4 streams 3.30 / 3.43)
+    st_tile = 1024 if args.window_streams > 1 else 512
+    w.tile_tokens = args.tile or (st_tile if args.staged else launch.get("tile", w.tile_tokens))
+    args.split = args.split or (st_tile if args.staged else launch.get("split", 0))
     overlap = args.overlap and not args.serial
     T = w.tile_tokens
     B, Hq, Hkv, D, L = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
@@ -333,6 +342,12 @@ def main():
     window = 32768 if args.staged else span
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, window, T, D, args.kernel, args.split)
     ws = torch.zeros(max(16, ws_bytes) // 4 + 4, dtype=torch.float32, device=dev)
+    # concurrent staged windows: one workspace and one stream each
+    n_ws = max(1, args.window_streams) if args.staged else 1
+    wss = [ws] + [torch.zeros_like(ws) for _ in range(n_ws - 1)]
+    wstreams = [None] + [torch.cuda.Stream() for _ in range(n_ws - 1)]
+    w_start = torch.cuda.Event()
+    w_done = [torch.cuda.Event() for _ in range(n_ws)]
     stream = torch.cuda.current_stream()
     merge_stream = torch.cuda.Stream()          # default priority
     decoded = [torch.cuda.Event() for _ in range(L)]
@@ -344,11 +359,20 @@ def main():
             pkv.decode_attention_rows(pool, layer, qs[layer], dt, dc, d_rt, max_row, max_tiles,
                                       w.scale, po[layer], pl[layer], stream=s)
             return
-        for begin in range(0, span, window):
+        if n_ws > 1:                       # windows round-robin over n_ws streams
+            w_start.record(s)
+            for ws_s in wstreams[1:]:
+                ws_s.wait_event(w_start)
+        for i, begin in enumerate(range(0, span, window)):
+            k = i % n_ws
             pkv.decode_attention(pool, layer, qs[layer], dt[:, begin // w.page_tokens:], dc,
                                  begin, min(window, span - begin), T, w.scale, po[layer],
-                                 pl[layer], workspace=ws, kernel=args.kernel,
-                                 split_tokens=args.split, stream=s)
+                                 pl[layer], workspace=wss[k], kernel=args.kernel,
+                                 split_tokens=args.split, stream=s if k == 0 else wstreams[k])
+        if n_ws > 1:                       # the merge waits for every window
+            for k in range(1, n_ws):
+                w_done[k].record(wstreams[k])
+                s.wait_event(w_done[k])
 
     # a whole-history fixed tiling decodes and merges each layer in one call
     # (one kernel boundary fewer where tiles hold several splits); the
@@ -441,6 +465,25 @@ def main():
         graph_res = time_graph(L, K, stream, use_merged, decode_layer, pkv, pool, qs, dt, dc,
                                span, T, w, po, pl, outs, lses, ws, args, timed_o, timed_l, same)
     timed_check = same(timed_o, outs) and same(timed_l, lses)
+    staged_vs_resident = None
+    if args.staged:
+        # one resident call over the whole history at the same tiling
+        ws_r = torch.zeros(max(16, pkv.decode_workspace_bytes(B, Hq, span, T, D, args.kernel,
+                                                              args.split)) // 4 + 4,
+                           dtype=torch.float32, device=dev)
+        staged_vs_resident = True
+        for layer in range(L):
+            rpo = torch.full_like(po[layer], float("nan"))
+            rpl = torch.full_like(pl[layer], float("nan"))
+            ro = torch.empty_like(outs[layer])
+            rl = torch.empty_like(lses[layer])
+            pkv.decode_attention(pool, layer, qs[layer], dt, dc, 0, span, T, w.scale, rpo, rpl,
+                                 workspace=ws_r, kernel=args.kernel, split_tokens=args.split,
+                                 stream=stream)
+            pkv.merge_partials(rpo, rpl, ro, rl, stream=stream)
+            torch.cuda.synchronize()
+            staged_vs_resident = (staged_vs_resident and same(ro, timed_o[layer])
+                                  and same(rl, timed_l[layer]))
 
     if args.host_staged and args.compact_older:
         res = host_staged_hybrid(args, w, pool, arena, table, ctx, qs, outs, lses, T, span)
@@ -486,7 +529,8 @@ def main():
                         f"{Hq} q / {Hkv} kv heads, head_dim {D}, 64-token pages, "
                         + (f"per-request tiles planned for {plan} work-groups (at most "
                            f"{max_row} tokens, {max_tiles} per request)" if plan else f"tile {T}")
-                        + (", staged 32768-token windows" if args.staged else ""),
+                        + (f", staged 32768-token windows ({n_ws} streams)" if args.staged
+                           else ""),
             "batch": B, "ctx_lens_sum": int(sum(w.ctx_lens)), "layers": L,
             "tile_tokens": row_tiles.tolist() if plan else T,
             "kernel": args.kernel, "split_tokens": args.split or "default",
@@ -524,6 +568,8 @@ def main():
         "overlapped_equals_serial_bitwise": self_check,
         **({"graph": graph_res} if graph_res is not None else {}),
         "timed_equals_serial_bitwise": timed_check,
+        **({"staged_equals_resident_bitwise": staged_vs_resident,
+            "window_streams": n_ws} if args.staged else {}),
         ("serial_merges" if overlap else "overlapped_merges"): {
             "ms_per_step": round(ms_other, 4),
             "value": round(kv_bytes_step / (ms_other * 1e-3) / 1e9, 1),
