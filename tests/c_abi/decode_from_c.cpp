@@ -1,7 +1,11 @@
 // The C ABI used from C++ with plain device pointers (no Python, no torch):
 // pool of an explicit size, page tables, the history written token by token
 // with pkv_append_kv, then pkv_decode_attention_merged and, for comparison,
-// pkv_decode_attention + pkv_merge_partials (which must give the same bits).
+// pkv_decode_attention + pkv_merge_partials (which must give the same bits),
+// and the per-step forms: the table written again from pinned host memory
+// with pkv_page_table_write_async (no host wait, an event recorded after the
+// copy) and decoded with pkv_decode_attention_merged_noalloc (no workspace):
+// the same bits once more.
 // Writes its inputs and results to the file named on the command line; the
 // test that runs it compares them with the float64 oracle.
 //
@@ -165,6 +169,40 @@ int main(int argc, char** argv) {
     std::fprintf(stderr, "merged decode and decode + merge differ\n");
     return 1;
   }
+
+  // the per-step forms: async table write from pinned memory, then the
+  // no-allocation merged decode, queued with no host wait in between
+  int32_t* h_table = nullptr;
+  int32_t* h_ctx = nullptr;
+  HIP_OK(hipHostMalloc(reinterpret_cast<void**>(&h_table), sizeof(int32_t) * B * pt_stride,
+                       hipHostMallocDefault));
+  HIP_OK(hipHostMalloc(reinterpret_cast<void**>(&h_ctx), sizeof(int32_t) * B,
+                       hipHostMallocDefault));
+  std::memcpy(h_table, table.data(), sizeof(int32_t) * B * pt_stride);
+  std::memcpy(h_ctx, ctx, sizeof(int32_t) * B);
+  HIP_OK(hipMemset(d_table, 0xFF, sizeof(int32_t) * B * pt_stride));   // forget the old table
+  HIP_OK(hipMemset(d_ctx, 0, sizeof(int32_t) * B));
+  hipEvent_t copied = nullptr;
+  HIP_OK(hipEventCreateWithFlags(&copied, hipEventDisableTiming));
+  if (int rc = pkv_page_table_write_async(pool, h_table, h_ctx, B, pt_stride, d_table, d_ctx,
+                                          nullptr, copied))
+    return fail_pkv("pkv_page_table_write_async", rc);
+  if (int rc = pkv_decode_attention_merged_noalloc(pool, 0, d_q, d_table, pt_stride, d_ctx, B,
+                                                   Hq, SLOTS * TILE, TILE, scale, d_po2, d_pl2,
+                                                   SLOTS, d_out2, d_lse2, &opts, nullptr))
+    return fail_pkv("pkv_decode_attention_merged_noalloc", rc);
+  HIP_OK(hipEventSynchronize(copied));       // the pinned table may be reused from here
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(out2.data(), d_out2, sizeof(float) * out2.size(), hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(lse2.data(), d_lse2, sizeof(float) * lse2.size(), hipMemcpyDeviceToHost));
+  if (std::memcmp(out.data(), out2.data(), 4 * out.size()) ||
+      std::memcmp(lse.data(), lse2.data(), 4 * lse.size())) {
+    std::fprintf(stderr, "async table + no-allocation decode differ from the merged decode\n");
+    return 1;
+  }
+  HIP_OK(hipEventDestroy(copied));
+  HIP_OK(hipHostFree(h_table));
+  HIP_OK(hipHostFree(h_ctx));
 
   FILE* f = std::fopen(argv[1], "wb");
   if (!f) {

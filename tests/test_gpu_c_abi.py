@@ -1,8 +1,9 @@
 """GPU: the C ABI used from C++ alone (tests/c_abi/decode_from_c.cpp, built
 by the package build): pool, page tables, the history written with
-pkv_append_kv, merged decode (checked there against decode + merge bit for
-bit), and the results here against the float64 oracle on the inputs the
-program wrote."""
+pkv_append_kv, merged decode (checked there against decode + merge, and
+against the asynchronous table write from pinned memory followed by the
+no-allocation merged decode, bit for bit), and the results here against
+the float64 oracle on the inputs the program wrote."""
 
 import os
 import subprocess
