@@ -82,7 +82,7 @@ typedef struct pkv_pool pkv_pool;   /* opaque host-side handle */
 const char* pkv_last_error(void);
 
 /* Library ABI version (PKV_ABI_VERSION). */
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 int32_t pkv_abi_version(void);
 
 /* Bytes of one physical page (all layers) for `geom`. */

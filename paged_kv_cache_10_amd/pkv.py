@@ -22,6 +22,8 @@ ERRORS = {
 KERNELS = {"default": 0, "valu": 1, "mfma": 2}
 
 # every symbol include/pkv.h declares
+ABI_VERSION = 4      # PKV_ABI_VERSION of the include/pkv.h this binding follows
+
 EXPORTS = [
     "pkv_last_error", "pkv_abi_version", "pkv_page_bytes", "pkv_pool_create", "pkv_pool_info",
     "pkv_pool_destroy", "pkv_page_table_validate", "pkv_page_table_write",
@@ -168,6 +170,10 @@ def lib():
         L.pkv_live_destroy.argtypes = [P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
+        got = L.pkv_abi_version()
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {got}, this binding is written for "
+                               f"{ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 

@@ -37,6 +37,12 @@ def test_library_exports_every_declared_symbol():
         assert getattr(L, n) is not None
 
 
+def test_abi_version_of_header_library_and_binding_agree():
+    hdr = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    v = int(re.search(r"#define PKV_ABI_VERSION (\d+)", hdr).group(1))
+    assert pkv.abi_version() == v == pkv.ABI_VERSION
+
+
 def geom(layers=16, hkv=4, d=256, pt=64):
     return pkv.Geom(layers, hkv, d, pt)
 
