@@ -82,7 +82,7 @@ typedef struct pkv_pool pkv_pool;   /* opaque host-side handle */
 const char* pkv_last_error(void);
 
 /* Library ABI version (PKV_ABI_VERSION). */
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 int32_t pkv_abi_version(void);
 
 /* Bytes of one physical page (all layers) for `geom`. */
@@ -617,6 +617,44 @@ int pkv_admit_destroy(pkv_admit* a);
  *   checked before anything is queued.
  * pkv_live_destroy waits for the three streams, then frees host state.  A
  *   HIP failure quarantines the runtime: every call but destroy is refused.
+ *
+ * Compact older pages in the live pool (KV-cache engineering, sections
+ * "Exact recent pages, compact older pages" and "What the hybrid tier
+ * buys": once the history is off the card the bus is the bound, and a
+ * representation is worth the bytes per token it stops moving).
+ * pkv_live_attach_compact (between steps, once)
+ *   cstage        compact (E4M3) pool, same KV heads: its num_layers C is the
+ *                 number of compact staging buffers (layer l uses buffer
+ *                 l % C), its num_pages the most compact pages one step may
+ *                 stage (more fails and quarantines the runtime).
+ *   compact_host  pinned host memory holding the compact copy of every host
+ *                 page in the layout of a compact pool of host_pages pages
+ *                 and L layers (codes [layer][page], then scales
+ *                 [layer][page]); compact_host_bytes exactly that size.
+ *   compact_tile_tokens  tile of the compact run: a multiple of 64 in
+ *                 64..16384 dividing pt_stride x 64.
+ *   dev_cstate    device int32 [max_batch * (pt_stride + 1)], the caller's:
+ *                 the compact run's table and lengths.
+ * pkv_live_publish / pkv_live_retract (host page ids, between steps): mark
+ *   host pages whose compact copy in compact_host is written (the caller
+ *   converts a page once it is full in every layer, e.g. with
+ *   pkv_compact_convert, and publishes it), or no longer valid.
+ * With compact pages attached, pkv_live_step_begin stages a page that is
+ *   not resident, full (all 64 tokens inside the length) and published as
+ *   compact: its entry in the composed table is -1 (the exact run masks
+ *   it), and it joins the request's compact run, in logical order, read
+ *   from a compact staging page.  Every other page is served as before.
+ *   info->compact_staged_pages counts them.  pkv_live_layer then copies the
+ *   compact pages' codes and scales of the layer after the last reader of
+ *   the buffer, and decodes both runs in one launch
+ *   (pkv_decode_attention_runs): the exact run over the composed table with
+ *   tiles of tile_tokens (opts.split_tokens 0 or tile_tokens; the other
+ *   options are ignored) into slots 0 .. E-1, E = pt_stride x 64 /
+ *   tile_tokens, the compact run into slots E .. E+C'-1, C' = pt_stride x
+ *   64 / compact_tile_tokens; num_slots must be E + C'.  Then
+ *   pkv_merge_partials into out and lse; workspace is unused.  The result
+ *   is bit-identical to pkv_decode_attention_runs + pkv_merge_partials over
+ *   resident copies of both runs.
  */
 typedef struct pkv_live pkv_live;
 typedef struct pkv_live_info {
@@ -624,6 +662,7 @@ typedef struct pkv_live_info {
   int64_t staged_pages;     /* pages staged for each layer this step */
   int32_t refused;          /* contexts refused this step */
   int32_t resident_pages;   /* pool pages the step reads */
+  int64_t compact_staged_pages;  /* pages staged as compact for each layer this step */
 } pkv_live_info;
 int pkv_live_create(const pkv_pool* pool, const pkv_pool* stage, void* host_arena,
                     uint64_t host_bytes, int32_t max_batch, int32_t pt_stride, int32_t* dev_state,
@@ -640,6 +679,11 @@ int pkv_live_layer(pkv_live* live, int32_t layer, const void* q, const void* k_n
                    const void* v_new, int32_t num_q_heads, int32_t tile_tokens, float scale,
                    float* part_out, float* part_lse, int32_t num_slots, float* out, float* lse,
                    void* workspace, uint64_t workspace_bytes, const pkv_decode_opts* opts);
+int pkv_live_attach_compact(pkv_live* live, const pkv_pool* cstage, void* compact_host,
+                            uint64_t compact_host_bytes, int32_t compact_tile_tokens,
+                            int32_t* dev_cstate);
+int pkv_live_publish(pkv_live* live, const int32_t* host_pages, int32_t n);
+int pkv_live_retract(pkv_live* live, const int32_t* host_pages, int32_t n);
 int pkv_live_destroy(pkv_live* live);
 
 #ifdef __cplusplus

@@ -641,10 +641,13 @@ PKV_API int pkv_decode_attention_merged_noalloc(const pkv_pool* pool, int32_t la
                      need > 0 ? (uint64_t)PKV_STATIC_SCRATCH_BYTES : 0, opts, stream, out, lse);
 }
 
-PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batch,
-                                      int32_t num_q_heads, const pkv_decode_run* runs,
-                                      int32_t n_runs, float scale, float* part_out,
-                                      float* part_lse, int32_t num_slots, void* stream) {
+namespace pkv {
+// pkv_decode_attention_runs with a layer of its own per run and, for an exact
+// run, a staging pool whose pages its table may name (the live pool's
+// composed table); with dry_run only the checks run.
+int runs_impl(const RunSpec* runs, int32_t n_runs, const void* q, int32_t batch,
+              int32_t num_q_heads, float scale, float* part_out, float* part_lse,
+              int32_t num_slots, void* stream, bool dry_run) {
   if (n_runs < 1 || n_runs > 2) return fail(PKV_ERR_INVALID_ARG, "n_runs = %d, need 1 or 2", n_runs);
   if (!runs) return fail(PKV_ERR_INVALID_ARG, "runs is NULL");
   if (batch < 0 || batch > 65535) return fail(PKV_ERR_INVALID_ARG, "batch = %d outside 0..65535", batch);
@@ -658,10 +661,11 @@ PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batc
   int group = 0;
   int lo[2] = {0, 0}, hi[2] = {0, 0};          // slots [lo, hi) of each run
   for (int k = 0; k < n_runs; ++k) {
-    const pkv_decode_run& u = runs[k];
+    const RunSpec& u = runs[k];
     if (!u.pool) return fail(PKV_ERR_INVALID_ARG, "runs[%d].pool is NULL", k);
     const pkv_pool* pool = u.pool;
     const pkv_geom& G = pool->geom;
+    const int32_t layer = u.layer;
     if (layer < 0 || layer >= G.num_layers)
       return fail(PKV_ERR_INVALID_ARG, "layer = %d outside 0..%d of runs[%d].pool", layer,
                   G.num_layers - 1, k);
@@ -702,6 +706,8 @@ PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batc
       return fail(PKV_ERR_INVALID_ARG, "runs[%d] holds %lld work-groups, more than %d", k,
                   (long long)wgs, INT32_MAX / 2);
     r.compact[k] = pool->format == PKV_FORMAT_E4M3;
+    if (u.stage && (r.compact[k] || u.stage->pool->format != PKV_FORMAT_BF16))
+      return fail(PKV_ERR_INVALID_ARG, "runs[%d]: staged pages are bf16 pages of an exact run", k);
     r.n_split[k] = n_tiles;
     r.wgs[k] = (int32_t)wgs;
     pkv::DecodeArgs& a = r.e[k];
@@ -724,6 +730,12 @@ PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batc
     a.out_lse = part_lse;
     a.out_slots = num_slots;
     a.out_slot0 = u.slot_offset;
+    if (u.stage) {
+      a.stage_arena = static_cast<const uint16_t*>(u.stage->pool->base);
+      a.stage_layer_off = (int64_t)(u.stage->pool->page_layer_bytes / 2) *
+                          u.stage->pool->num_pages * u.stage->layer;
+      a.stage_pages = (int32_t)u.stage->pool->num_pages;
+    }
     if (r.compact[k]) {
       pkv::CompactDecodeArgs& c = r.c[k];
       c.codes = static_cast<const uint8_t*>(pool->base);
@@ -757,9 +769,25 @@ PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batc
     return fail(PKV_ERR_INVALID_ARG, "q, part_out or part_lse is NULL");
   if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(part_out) % 16)
     return fail(PKV_ERR_INVALID_ARG, "q and part_out must be 16-byte aligned");
+  if (dry_run) return ok();
   hipError_t e = pkv::launch_decode_runs(r, group, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace pkv
+
+PKV_API int pkv_decode_attention_runs(int32_t layer, const void* q, int32_t batch,
+                                      int32_t num_q_heads, const pkv_decode_run* runs,
+                                      int32_t n_runs, float scale, float* part_out,
+                                      float* part_lse, int32_t num_slots, void* stream) {
+  if (n_runs < 1 || n_runs > 2) return fail(PKV_ERR_INVALID_ARG, "n_runs = %d, need 1 or 2", n_runs);
+  if (!runs) return fail(PKV_ERR_INVALID_ARG, "runs is NULL");
+  pkv::RunSpec spec[2];
+  for (int k = 0; k < n_runs; ++k)
+    spec[k] = {runs[k].pool, layer, runs[k].dev_table, runs[k].pt_stride, runs[k].dev_ctx_lens,
+               runs[k].token_count, runs[k].tile_tokens, runs[k].slot_offset, nullptr};
+  return pkv::runs_impl(spec, n_runs, q, batch, num_q_heads, scale, part_out, part_lse, num_slots,
+                        stream, false);
 }
 
 PKV_API int pkv_plan_tiles(const int32_t* host_ctx_lens, int32_t batch, int32_t num_kv_heads,

@@ -29,6 +29,16 @@
 //   write-back       waits for the decode; stores the new token's K and V
 //                    rows into the host pages (the changed rows only).
 // The host waits only when the table ring is full and in destroy.
+//
+// With compact pages attached (KV-cache engineering, sections "Exact recent
+// pages, compact older pages" and "What the hybrid tier buys": a
+// representation is judged by the bytes per token it stops moving), a
+// non-resident page whose compact copy the caller has published is staged
+// as E4M3 codes and scales instead of bf16: its entry in the exact table is
+// -1 and it joins a compact run of its own (logical order, every page full).
+// The layer's decode is then one launch of both runs (the exact run over
+// the composed table, the compact run from the compact staging pool) into
+// disjoint slots, and one FP32 merge.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -89,6 +99,16 @@ struct pkv_live {
   std::vector<PageCopy> staged;         // staging pages to fill from the host
   std::vector<pkv::TailRow> tails;      // new token rows to write back
   bool quarantined = false;
+  // compact older pages (attached or not)
+  const pkv_pool* cstage = nullptr;     // E4M3 staging pool: its layers are the buffers
+  int32_t* dev_cstate = nullptr;        // [max_batch][pt_stride] compact table, [max_batch] lengths
+  char* chost = nullptr;                // compact host arena: codes [layer][page], then scales
+  uint64_t chost_scale_off = 0;
+  int32_t ctile = 0;                    // tile tokens of the compact run
+  std::vector<char> published;          // per host page: a compact copy exists
+  std::vector<PageCopy> cstaged;        // compact staging page <- host page
+  std::vector<hipEvent_t> cbuf_done;    // after the write-back of the last layer using it
+  std::vector<char> cbuf_done_set;
 };
 
 namespace {
@@ -132,6 +152,7 @@ void destroy_events(pkv_live* L) {
   if (L->consumed) (void)hipEventDestroy(L->consumed);
   for (auto ev : L->layer_done) if (ev) (void)hipEventDestroy(ev);
   for (auto ev : L->buf_done) if (ev) (void)hipEventDestroy(ev);
+  for (auto ev : L->cbuf_done) if (ev) (void)hipEventDestroy(ev);
 }
 
 }  // namespace
@@ -187,7 +208,8 @@ PKV_API int pkv_live_create(const pkv_pool* pool, const pkv_pool* stage, void* h
   void* dev = nullptr;
   hipError_t e = hipHostGetDevicePointer(&dev, host_arena, 0);
   L->host_dev = static_cast<char*>(dev);
-  const size_t slot = (size_t)max_batch * (size_t)(pt_stride + 2);
+  // each ring slot: the dev_state image, then the compact run's table and lengths
+  const size_t slot = (size_t)max_batch * (size_t)(2 * pt_stride + 3);
   if (e == hipSuccess)
     e = hipHostMalloc(reinterpret_cast<void**>(&L->ring), sizeof(int32_t) * slot * kRing,
                       hipHostMallocDefault);
@@ -246,6 +268,75 @@ PKV_API int pkv_live_admission(pkv_live* L, pkv_admit** out) {
   return PKV_OK;
 }
 
+PKV_API int pkv_live_attach_compact(pkv_live* L, const pkv_pool* cstage, void* compact_host,
+                                    uint64_t compact_host_bytes, int32_t compact_tile_tokens,
+                                    int32_t* dev_cstate) {
+  if (!L || !cstage || !compact_host || !dev_cstate)
+    return fail(PKV_ERR_INVALID_ARG, "live pool, cstage, compact_host or dev_cstate is NULL");
+  if (L->cstage) return fail(PKV_ERR_INVALID_ARG, "compact pages are already attached");
+  if (L->open) return fail(PKV_ERR_LEASE, "a step is open: attach between steps");
+  if (cstage->format != PKV_FORMAT_E4M3)
+    return fail(PKV_ERR_INVALID_ARG, "cstage must be a compact (E4M3) pool");
+  if (cstage->geom.num_kv_heads != L->pool->geom.num_kv_heads)
+    return fail(PKV_ERR_GEOMETRY, "the compact staging pool's KV heads differ from the pool's");
+  const uint64_t cplb = cstage->page_layer_bytes;                  // codes of one (layer, page)
+  const uint64_t csb = 2ull * (uint64_t)cstage->geom.num_kv_heads * 4ull;
+  const uint64_t want = (cplb + csb) * (uint64_t)L->layers * (uint64_t)L->host_pages;
+  if (compact_host_bytes != want)
+    return pkv::set_error(PKV_ERR_INVALID_ARG,
+                          "compact_host_bytes = %llu; the compact copy of %lld host pages of %d "
+                          "layers takes %llu", (unsigned long long)compact_host_bytes,
+                          (long long)L->host_pages, L->layers, (unsigned long long)want);
+  const int PT = L->pool->geom.page_tokens;
+  if (compact_tile_tokens < PT || compact_tile_tokens > 64 * 4 * PT || compact_tile_tokens % PT ||
+      ((int64_t)L->pt_stride * PT) % compact_tile_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "compact_tile_tokens must be a multiple of 64 in 64..16384 "
+                "that divides pt_stride x 64");
+  if ((int64_t)L->pool->num_pages + cstage->num_pages > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "too many pages");
+  L->cbuf_done.assign((size_t)cstage->geom.num_layers, nullptr);
+  L->cbuf_done_set.assign((size_t)cstage->geom.num_layers, 0);
+  hipError_t e = hipSuccess;
+  for (auto& ev : L->cbuf_done)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    for (auto& ev : L->cbuf_done) if (ev) (void)hipEventDestroy(ev);
+    L->cbuf_done.clear();
+    return pkv::set_error(PKV_ERR_DEVICE, "attach failed: %s", hipGetErrorString(e));
+  }
+  L->cstage = cstage;
+  L->dev_cstate = dev_cstate;
+  L->chost = static_cast<char*>(compact_host);
+  L->chost_scale_off = cplb * (uint64_t)L->layers * (uint64_t)L->host_pages;
+  L->ctile = compact_tile_tokens;
+  L->published.assign((size_t)L->host_pages, 0);
+  pkv::clear_error();
+  return PKV_OK;
+}
+
+namespace {
+int set_published(pkv_live* L, const int32_t* host_pages, int32_t n, char value) {
+  if (!L) return fail(PKV_ERR_INVALID_ARG, "live pool is NULL");
+  if (!L->cstage) return fail(PKV_ERR_INVALID_ARG, "no compact pages are attached");
+  if (n < 0 || (n > 0 && !host_pages)) return fail(PKV_ERR_INVALID_ARG, "bad host page list");
+  for (int32_t i = 0; i < n; ++i)
+    if (host_pages[i] < 0 || host_pages[i] >= L->host_pages)
+      return pkv::set_error(PKV_ERR_INVALID_ARG, "host_pages[%d] = %d is not a host page", i,
+                            host_pages[i]);
+  for (int32_t i = 0; i < n; ++i) L->published[(size_t)host_pages[i]] = value;
+  pkv::clear_error();
+  return PKV_OK;
+}
+}  // namespace
+
+PKV_API int pkv_live_publish(pkv_live* L, const int32_t* host_pages, int32_t n) {
+  return set_published(L, host_pages, n, 1);
+}
+
+PKV_API int pkv_live_retract(pkv_live* L, const int32_t* host_pages, int32_t n) {
+  return set_published(L, host_pages, n, 0);
+}
+
 PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
                                 const int64_t* lengths, const int32_t* host_rows,
                                 int32_t host_stride, int32_t* status, pkv_live_info* info) {
@@ -285,12 +376,18 @@ PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
   if (rc != PKV_OK) return rc;
   // compose the step's table; hot pages and staged pages
   const int32_t P = (int32_t)L->pool->num_pages;
-  const size_t slot = (size_t)L->max_batch * (size_t)(L->pt_stride + 2);
+  const size_t slot = (size_t)L->max_batch * (size_t)(2 * L->pt_stride + 3);
+  const size_t state = (size_t)L->max_batch * (size_t)(L->pt_stride + 2);
   int32_t* tab = L->ring + slot * (size_t)k;
   int32_t* lens = tab + (size_t)L->max_batch * L->pt_stride;
   int32_t* pos = lens + L->max_batch;
+  int32_t* ctab = pos + L->max_batch;                    // the compact run's rows
+  int32_t* clens = ctab + (size_t)L->max_batch * L->pt_stride;
+  std::fill(ctab, ctab + (size_t)L->max_batch * L->pt_stride, -1);
+  std::fill(clens, clens + L->max_batch, 0);
   L->hot.clear();
   L->staged.clear();
+  L->cstaged.clear();
   L->tails.clear();
   int32_t refused = 0, resident = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -305,8 +402,23 @@ PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
       continue;
     }
     const int32_t need = (int32_t)((lengths[i] + PT - 1) / PT);
+    int32_t nc = 0;
     for (int32_t lp = 0; lp < need; ++lp) {
       const int32_t d = arow[lp];
+      const bool full = (int64_t)(lp + 1) * PT <= lengths[i];
+      if (d < 0 && L->cstage && full && L->published[(size_t)hrow[lp]]) {   // staged compact
+        const int32_t c = (int32_t)L->cstaged.size();
+        if (c >= L->cstage->num_pages) {
+          L->quarantined = true;
+          return pkv::set_error(PKV_ERR_PAGE_TABLE,
+                                "the step stages more than the compact staging pool's %lld "
+                                "pages; raise it (live pool quarantined)",
+                                (long long)L->cstage->num_pages);
+        }
+        L->cstaged.push_back({c, hrow[lp]});
+        ctab[(size_t)i * L->pt_stride + nc++] = c;
+        continue;                                        // its exact entry stays -1
+      }
       if (d >= 0) {
         out[lp] = d;
         ++resident;
@@ -334,6 +446,7 @@ PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
     }
     lens[i] = (int32_t)lengths[i];
     pos[i] = (int32_t)lengths[i] - 1;
+    clens[i] = nc * PT;
     L->tails.push_back({arow[tail], hrow[tail], (int32_t)((lengths[i] - 1) % PT), 0});
   }
   for (int32_t i = n; i < L->max_batch; ++i) {
@@ -342,8 +455,11 @@ PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
     pos[i] = -1;
   }
   // the table, lengths and positions to the device, in stream order
-  hipError_t e = hipMemcpyAsync(L->dev_state, tab, sizeof(int32_t) * slot, hipMemcpyHostToDevice,
-                                L->compute);
+  hipError_t e = hipMemcpyAsync(L->dev_state, tab, sizeof(int32_t) * state,
+                                hipMemcpyHostToDevice, L->compute);
+  if (e == hipSuccess && L->cstage)
+    e = hipMemcpyAsync(L->dev_cstate, ctab, sizeof(int32_t) * (slot - state),
+                       hipMemcpyHostToDevice, L->compute);
   if (e == hipSuccess) e = hipEventRecord(L->ring_ev[k], L->compute);
   if (e != hipSuccess) return quarantine(L, e, "table copy");
   L->ring_used[k] = true;
@@ -355,6 +471,7 @@ PKV_API int pkv_live_step_begin(pkv_live* L, int32_t n, const int32_t* ctx_ids,
   if (info) {
     info->copied_in_pages = (int64_t)L->hot.size();
     info->staged_pages = (int64_t)L->staged.size();
+    info->compact_staged_pages = (int64_t)L->cstaged.size();
     info->refused = refused;
     info->resident_pages = resident;
   }
@@ -374,21 +491,51 @@ PKV_API int pkv_live_layer(pkv_live* L, int32_t layer, const void* q, const void
   if (L->layer_run[(size_t)layer])
     return pkv::set_error(PKV_ERR_LEASE, "layer %d already ran in this step", layer);
   if (!k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "k_new or v_new is NULL");
-  if ((int64_t)num_slots * tile_tokens > (int64_t)L->pt_stride * L->pool->geom.page_tokens)
+  if (!L->cstage &&
+      (int64_t)num_slots * tile_tokens > (int64_t)L->pt_stride * L->pool->geom.page_tokens)
     return fail(PKV_ERR_INVALID_ARG, "num_slots x tile_tokens exceeds the table's pages");
   if (reinterpret_cast<uintptr_t>(k_new) % 16)
     return fail(PKV_ERR_INVALID_ARG, "k_new must be 16-byte aligned");
   const int32_t* dev_table = L->dev_state;
   const int32_t* dev_lens = dev_table + (size_t)L->max_batch * L->pt_stride;
   const int32_t* dev_pos = dev_lens + L->max_batch;
+  const int32_t* dev_ctable = L->dev_cstate;
+  const int32_t* dev_clens = dev_ctable + (size_t)L->max_batch * L->pt_stride;
   const int32_t buf = layer % L->buffers;
   const pkv::StageRef st{L->stage, buf};
-  // every argument of the decode checked before anything is queued
-  if (int rc = pkv::decode_merged_staged(L->pool, layer, q, dev_table, L->pt_stride, dev_lens,
-                                         L->n, num_q_heads, num_slots * tile_tokens, tile_tokens,
-                                         scale, part_out, part_lse, num_slots, out, lse,
-                                         workspace, workspace_bytes, opts, L->compute, st, true))
-    return rc;
+  // with compact pages: both runs in one launch (exact tiles first, then the
+  // compact run's), one merge over every slot
+  const int PTk = L->pool->geom.page_tokens;
+  const int32_t cbuf = L->cstage ? layer % L->cstage->geom.num_layers : 0;
+  pkv::RunSpec runs[2];
+  int32_t n_exact = 0;
+  if (L->cstage) {
+    if (tile_tokens <= 0 || ((int64_t)L->pt_stride * PTk) % tile_tokens)
+      return fail(PKV_ERR_INVALID_ARG, "tile_tokens must divide pt_stride x 64 with compact pages");
+    if (opts && opts->split_tokens != 0 && opts->split_tokens != tile_tokens)
+      return fail(PKV_ERR_INVALID_ARG, "with compact pages every exact tile is one split");
+    n_exact = L->pt_stride * PTk / tile_tokens;
+    const int32_t n_compact = L->pt_stride * PTk / L->ctile;
+    if (num_slots != n_exact + n_compact)
+      return pkv::set_error(PKV_ERR_INVALID_ARG, "num_slots = %d; with compact pages it is %d "
+                            "exact tiles + %d compact tiles", num_slots, n_exact, n_compact);
+    runs[0] = {L->pool, layer, dev_table, L->pt_stride, dev_lens, n_exact * tile_tokens,
+               tile_tokens, 0, &st};
+    runs[1] = {L->cstage, cbuf, dev_ctable, L->pt_stride, dev_clens, n_compact * L->ctile,
+               L->ctile, n_exact, nullptr};
+    if (int rc = pkv::runs_impl(runs, 2, q, L->n, num_q_heads, scale, part_out, part_lse,
+                                num_slots, L->compute, true))
+      return rc;
+    if (!out || !lse || reinterpret_cast<uintptr_t>(out) % 16)
+      return fail(PKV_ERR_INVALID_ARG, "out or lse is NULL, or out is not 16-byte aligned");
+  } else if (int rc = pkv::decode_merged_staged(L->pool, layer, q, dev_table, L->pt_stride,
+                                                dev_lens, L->n, num_q_heads,
+                                                num_slots * tile_tokens, tile_tokens, scale,
+                                                part_out, part_lse, num_slots, out, lse,
+                                                workspace, workspace_bytes, opts, L->compute, st,
+                                                true)) {
+    return rc;                           // every argument checked before anything is queued
+  }
   const uint64_t plb = L->pool->page_layer_bytes;
   // 1. copies of this layer's hot and staged pages, after their last readers
   hipError_t e = hipSuccess;
@@ -397,12 +544,29 @@ PKV_API int pkv_live_layer(pkv_live* L, int32_t layer, const void* q, const void
       e = hipStreamWaitEvent(cs, L->layer_done[(size_t)layer], 0);
     if (e == hipSuccess && L->buf_done_set[(size_t)buf])
       e = hipStreamWaitEvent(cs, L->buf_done[(size_t)buf], 0);
+    if (e == hipSuccess && L->cstage && L->cbuf_done_set[(size_t)cbuf])
+      e = hipStreamWaitEvent(cs, L->cbuf_done[(size_t)cbuf], 0);
   }
   const char* hslab = L->host + (uint64_t)layer * (uint64_t)L->host_pages * plb;
   char* pslab = static_cast<char*>(L->pool->base) + (uint64_t)layer * (uint64_t)L->pool->num_pages * plb;
   char* sslab = static_cast<char*>(L->stage->base) + (uint64_t)buf * (uint64_t)L->stage->num_pages * plb;
   if (e == hipSuccess) e = copy_pages(L->hot, pslab, hslab, plb, L->copy, L->copy2);
   if (e == hipSuccess) e = copy_pages(L->staged, sslab, hslab, plb, L->copy, L->copy2);
+  if (e == hipSuccess && L->cstage && !L->cstaged.empty()) {
+    // compact pages: codes (two halves on two engines) and scales of this layer
+    const uint64_t cplb = L->cstage->page_layer_bytes;
+    const uint64_t csb = 2ull * (uint64_t)L->cstage->geom.num_kv_heads * 4ull;
+    const uint64_t cpages = (uint64_t)L->cstage->num_pages;
+    char* cbase = static_cast<char*>(L->cstage->base);
+    e = copy_pages(L->cstaged, cbase + (uint64_t)cbuf * cpages * cplb,
+                   L->chost + (uint64_t)layer * (uint64_t)L->host_pages * cplb, cplb, L->copy,
+                   L->copy2);
+    if (e == hipSuccess)
+      e = copy_pages(L->cstaged, cbase + L->cstage->scale_offset + (uint64_t)cbuf * cpages * csb,
+                     L->chost + L->chost_scale_off +
+                         (uint64_t)layer * (uint64_t)L->host_pages * csb,
+                     csb, L->copy, L->copy2);
+  }
   if (e == hipSuccess) e = hipEventRecord(L->copied, L->copy);
   if (e == hipSuccess) e = hipEventRecord(L->copied2, L->copy2);
   if (e == hipSuccess) e = hipStreamWaitEvent(L->compute, L->copied, 0);
@@ -411,7 +575,13 @@ PKV_API int pkv_live_layer(pkv_live* L, int32_t layer, const void* q, const void
   // 2. append the new token, decode over the composed table, merge
   int rc = pkv_append_kv(L->pool, layer, dev_table, L->pt_stride, dev_pos, L->n, k_new, v_new,
                          L->compute);
-  if (rc == PKV_OK) {
+  if (rc == PKV_OK && L->cstage) {
+    rc = pkv::runs_impl(runs, 2, q, L->n, num_q_heads, scale, part_out, part_lse, num_slots,
+                        L->compute, false);
+    if (rc == PKV_OK)
+      rc = pkv_merge_partials(part_out, part_lse, L->n * num_q_heads, num_slots,
+                              L->pool->geom.head_dim, out, lse, L->compute);
+  } else if (rc == PKV_OK) {
     rc = pkv::decode_merged_staged(L->pool, layer, q, dev_table, L->pt_stride, dev_lens, L->n,
                                    num_q_heads, num_slots * tile_tokens, tile_tokens, scale,
                                    part_out, part_lse, num_slots, out, lse, workspace,
@@ -442,9 +612,11 @@ PKV_API int pkv_live_layer(pkv_live* L, int32_t layer, const void* q, const void
   }
   if (e == hipSuccess) e = hipEventRecord(L->layer_done[(size_t)layer], L->writeback);
   if (e == hipSuccess) e = hipEventRecord(L->buf_done[(size_t)buf], L->writeback);
+  if (e == hipSuccess && L->cstage) e = hipEventRecord(L->cbuf_done[(size_t)cbuf], L->writeback);
   if (e != hipSuccess) return quarantine(L, e, "layer write-back");
   L->layer_done_set[(size_t)layer] = 1;
   L->buf_done_set[(size_t)buf] = 1;
+  if (L->cstage) L->cbuf_done_set[(size_t)cbuf] = 1;
   L->layer_run[(size_t)layer] = 1;
   if (++L->layers_run == L->layers) L->open = false;     // every layer queued: the step is done
   pkv::clear_error();

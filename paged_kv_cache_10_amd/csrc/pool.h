@@ -37,4 +37,22 @@ int decode_merged_staged(const pkv_pool* pool, int32_t layer, const void* q,
                          int32_t num_slots, float* out, float* lse, void* workspace,
                          uint64_t workspace_bytes, const pkv_decode_opts* opts, void* stream,
                          const StageRef& stage, bool dry_run = false);
+
+// One run of pkv_decode_attention_runs, with a layer of its own and, for an
+// exact run, a staging pool its table may name.
+struct RunSpec {
+  const pkv_pool* pool;
+  int32_t layer;
+  const int32_t* dev_table;
+  int32_t pt_stride;
+  const int32_t* dev_ctx_lens;
+  int32_t token_count;
+  int32_t tile_tokens;
+  int32_t slot_offset;
+  const StageRef* stage;
+};
+
+int runs_impl(const RunSpec* runs, int32_t n_runs, const void* q, int32_t batch,
+              int32_t num_q_heads, float scale, float* part_out, float* part_lse,
+              int32_t num_slots, void* stream, bool dry_run);
 }  // namespace pkv

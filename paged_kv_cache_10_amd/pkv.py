@@ -22,7 +22,7 @@ ERRORS = {
 KERNELS = {"default": 0, "valu": 1, "mfma": 2}
 
 # every symbol include/pkv.h declares
-ABI_VERSION = 4      # PKV_ABI_VERSION of the include/pkv.h this binding follows
+ABI_VERSION = 5      # PKV_ABI_VERSION of the include/pkv.h this binding follows
 
 EXPORTS = [
     "pkv_last_error", "pkv_abi_version", "pkv_page_bytes", "pkv_pool_create", "pkv_pool_info",
@@ -39,6 +39,7 @@ EXPORTS = [
     "pkv_page_table_write_async",
     "pkv_live_create", "pkv_live_add", "pkv_live_set_target", "pkv_live_remove",
     "pkv_live_admission", "pkv_live_step_begin", "pkv_live_layer", "pkv_live_destroy",
+    "pkv_live_attach_compact", "pkv_live_publish", "pkv_live_retract",
 ]
 
 
@@ -168,6 +169,9 @@ def lib():
         L.pkv_live_layer.argtypes = [P, I32, P, P, P, I32, I32, ctypes.c_float, P, P, I32, P, P,
                                      P, U64, ctypes.POINTER(DecodeOpts)]
         L.pkv_live_destroy.argtypes = [P]
+        L.pkv_live_attach_compact.argtypes = [P, P, P, U64, I32, P]
+        L.pkv_live_publish.argtypes = [P, I32P, I32]
+        L.pkv_live_retract.argtypes = [P, I32P, I32]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         got = L.pkv_abi_version()
@@ -637,7 +641,8 @@ class Admission:
 
 class LiveInfo(ctypes.Structure):
     _fields_ = [("copied_in_pages", ctypes.c_int64), ("staged_pages", ctypes.c_int64),
-                ("refused", ctypes.c_int32), ("resident_pages", ctypes.c_int32)]
+                ("refused", ctypes.c_int32), ("resident_pages", ctypes.c_int32),
+                ("compact_staged_pages", ctypes.c_int64)]
 
 
 class Live:
@@ -717,6 +722,37 @@ class Live:
                                     _ptr(out, torch.float32, "out"),
                                     _ptr(lse, torch.float32, "lse"), ws_ptr, ws_bytes,
                                     ctypes.byref(o)))
+
+    def attach_compact(self, cstage_pool, compact_host, compact_tile_tokens):
+        """Compact older pages: `compact_host` (pinned) holds every host
+        page's compact copy in the layout of a compact pool of the host's
+        pages; `cstage_pool` (E4M3) stages them, its layers the buffers."""
+        import torch
+        if not compact_host.is_pinned():
+            raise ValueError("compact_host must be pinned host memory")
+        self.cstage_pool, self.compact_host = cstage_pool, compact_host
+        self.dev_cstate = torch.full((self.max_batch * (self.pt_stride + 1),), -1,
+                                     dtype=torch.int32, device="cuda")
+        _check(lib().pkv_live_attach_compact(self.handle, cstage_pool.handle,
+                                             compact_host.data_ptr(),
+                                             compact_host.numel() * compact_host.element_size(),
+                                             int(compact_tile_tokens),
+                                             self.dev_cstate.data_ptr()))
+        self.compact_tile_tokens = int(compact_tile_tokens)
+
+    def publish(self, host_pages):
+        a, p = _i32_array(host_pages)
+        _check(lib().pkv_live_publish(self.handle, p, len(a)))
+
+    def retract(self, host_pages):
+        a, p = _i32_array(host_pages)
+        _check(lib().pkv_live_retract(self.handle, p, len(a)))
+
+    def compact_table(self, n):
+        """The open step's compact-run table and lengths (device)."""
+        t = self.dev_cstate[:self.max_batch * self.pt_stride].view(self.max_batch, self.pt_stride)
+        lens = self.dev_cstate[self.max_batch * self.pt_stride:]
+        return t[:n], lens[:n]
 
     def table(self, n):
         """The open step's composed table, lengths and positions (device)."""

@@ -55,4 +55,8 @@ def test_calls_on_no_runtime_are_refused():
     assert L.pkv_live_step_begin(None, 1, None, None, None, 1, st, None) == -1
     assert L.pkv_live_layer(None, 0, None, None, None, 24, 1024, 0.0625, None, None, 1, None,
                             None, None, 0, None) == -1
+    assert L.pkv_live_attach_compact(None, None, None, 0, 1024, None) == -1
+    pages = (ctypes.c_int32 * 1)(0)
+    assert L.pkv_live_publish(None, pages, 1) == -1
+    assert L.pkv_live_retract(None, pages, 1) == -1
     assert L.pkv_live_destroy(None) == 0
