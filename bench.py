@@ -246,6 +246,10 @@ def parse():
     ap.add_argument("--live", action="store_true",
                     help="the live pool: four ~31,744-token requests growing by one token per "
                          "step, device pool 3/4 of the pages, histories in pinned host memory")
+    ap.add_argument("--live-compact", action="store_true",
+                    help="the live pool with compact older pages: every page not resident is "
+                         "staged as E4M3 codes and scales (half the bus bytes) and decoded as a "
+                         "second run in the same launch")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the timed step in a HIP graph and time its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -270,7 +274,7 @@ def main():
     if args.merge_stress:
         print(json.dumps(merge_stress(args, ceiling)), flush=True)
         return 0
-    if args.live:
+    if args.live or args.live_compact:
         print(json.dumps(live_pool(args)), flush=True)
         return 0
     import torch
@@ -741,19 +745,28 @@ def live_pool(args):
     schedule of the GPU test (targets change, a request pauses), every layer
     checked bitwise against a resident decode; then `steps` timed steps with
     all four requests growing, against the resident decode of the same
-    histories."""
+    histories.
+
+    With --live-compact every page full in the final histories has a compact
+    copy (converted once on the GPU, kept in pinned host memory) published
+    from the start, so each page the pool does not hold is staged compact:
+    the exact run (2,048-token tiles over the composed table, compact pages
+    masked) and the compact run (2,048-token tiles) in one launch, then one
+    merge.  Checked bitwise against the same two runs over resident copies
+    (tables read back after each schedule step)."""
     import torch
     from paged_kv_cache_10_amd import inputs as I
     from paged_kv_cache_10_amd import pkv
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    compact = bool(args.live_compact)
     sc = I.live_schedule(20)
     grow = args.warmup + args.steps
     final = [f + grow for f in sc["final"]]
     W = I.Workload("live", seed=81, ctx_lens=final, num_layers=16, tile_tokens=8192)
     L, Hq, Hkv, D, PT = W.num_layers, W.num_q_heads, W.num_kv_heads, W.head_dim, W.page_tokens
-    T, SPLIT = 8192, 2048
-    width = 4 * T // PT
+    width = 4 * 8192 // PT
+    T, SPLIT, CT = (2048, 0, 2048) if compact else (8192, 2048, 0)
     npg = [-(-c // PT) for c in final]
     bases = np.concatenate([[0], np.cumsum(npg)[:-1]]).astype(np.int64)
     Ph = int(sum(npg))
@@ -786,8 +799,27 @@ def live_pool(args):
     live = pkv.Live(pool, spool, host, W.batch, width, copy_s, compute, wb_s)
     for c, (t, bu) in sc["contexts"].items():
         live.add(c, t, bu)
-    S = 4
-    nbw = pkv.decode_workspace_bytes(W.batch, Hq, S * T, T, D, 0, SPLIT)
+    E = width * PT // T
+    CS = width * PT // CT if compact else 0
+    S = E + CS
+    if compact:
+        cpb = pkv.compact_page_bytes(L, Hkv)
+        cfull_arena = torch.zeros(Ph * cpb, dtype=torch.uint8, device=dev)
+        cfull = pkv.Pool(cfull_arena, L, Hkv, compact=True)
+        full_pages = np.concatenate([bases[b] + np.arange(c // PT)
+                                     for b, c in enumerate(final)]).astype(np.int32)
+        ids_dev = torch.from_numpy(full_pages).to(dev)
+        crc = torch.zeros(ids_dev.numel(), dtype=torch.int32, device=dev)
+        pkv.compact_convert(rpool, cfull, ids_dev, ids_dev, crc)
+        torch.cuda.synchronize()
+        chost = torch.empty(cfull_arena.numel(), dtype=torch.uint8, pin_memory=True)
+        chost.copy_(cfull_arena)
+        carena = torch.zeros(K_BUF * Ph * cpb // L, dtype=torch.uint8, device=dev)
+        cstage = pkv.Pool(carena, K_BUF, Hkv, compact=True)
+        live.attach_compact(cstage, chost, CT)
+        live.publish(full_pages)
+        cplb_all = cpb // L                      # codes and scales of one (layer, page)
+    nbw = pkv.decode_workspace_bytes(W.batch, Hq, E * T, T, D, 0, SPLIT or T)
     ws = torch.zeros(max(16, nbw) // 4 + 4, device=dev)
     ws_r = torch.zeros_like(ws)
     po = torch.empty((L, W.batch, Hq, S, D), device=dev)
@@ -809,9 +841,36 @@ def live_pool(args):
                        outs[layer, :n], lses[layer, :n], workspace=ws, split_tokens=SPLIT)
         return status, info
 
-    def resident_step(ids, lens):
+    def resident_tables(ids, lens):
+        """With compact pages: the open step's composition read back, as
+        tables over resident copies (the exact run masked where the page is
+        compact, the compact run naming host pages = compact copies)."""
+        n = len(ids)
+        comp = live.table(n)[0].cpu().numpy()
+        clen = live.compact_table(n)[1].cpu().numpy()
+        ref_e = table[ids].copy()
+        ref_c = np.full((n, width), -1, np.int32)
+        for i, ln in enumerate(lens):
+            need = -(-ln // PT)
+            lps = np.nonzero(comp[i, :need] == -1)[0]
+            ref_e[i, lps] = -1
+            ref_c[i, :lps.size] = table[ids[i], lps]
+        return (torch.from_numpy(ref_e).to(dev), torch.from_numpy(ref_c).to(dev),
+                torch.from_numpy(clen.astype(np.int32)).to(dev))
+
+    def resident_step(ids, lens, tabs=None):
         n = len(ids)
         dl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        if compact:
+            de, dc, dcl = tabs
+            for layer in range(L):
+                pkv.decode_attention_runs(layer, qs[layer][:n],
+                                          [(rpool, de, dl, E * T, T, 0),
+                                           (cfull, dc, dcl, CS * CT, CT, E)],
+                                          W.scale, rpo[layer, :n], rpl[layer, :n])
+                pkv.merge_partials(rpo[layer, :n], rpl[layer, :n], routs[layer, :n],
+                                   rlses[layer, :n])
+            return
         rows = dev_rtab[ids].contiguous()
         for layer in range(L):
             pkv.decode_attention_merged(rpool, layer, qs[layer][:n], rows, dl, S * T, T, W.scale,
@@ -830,7 +889,7 @@ def live_pool(args):
         for c, ln in zip(ids, lens):
             length[c] = ln
         live_step(ids, lens)
-        resident_step(ids, lens)
+        resident_step(ids, lens, resident_tables(ids, lens) if compact else None)
         torch.cuda.synchronize()
         n = len(ids)
         ok = ok and all(same(x[:, :n], y[:, :n]) for x, y in
@@ -864,10 +923,12 @@ def live_pool(args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     timed = infos[first:]
-    # the resident decode of the same histories, same tiling
+    # the resident decode of the same histories, same tiling (with compact
+    # pages: the last timed step's composition for every step)
+    tabs = resident_tables(ids, lens_timed[-1]) if compact else None
     e0.record(compute)
     for lens in lens_timed:
-        resident_step(ids, lens)
+        resident_step(ids, lens, tabs)
     e1.record(compute)
     torch.cuda.synchronize()
     ms_res = e0.elapsed_time(e1) / args.steps
@@ -875,27 +936,38 @@ def live_pool(args):
     ceiling = h2d_ceiling_GBs(host, dev, compute, copy_s)
     staged = float(np.mean([i["staged_pages"] for i in timed]))
     hot = float(np.mean([i["copied_in_pages"] for i in timed]))
+    cstaged = float(np.mean([i["compact_staged_pages"] for i in timed]))
     kv = float(np.mean([sum(x) for x in lens_timed])) * 4096 * L
     h2d = (staged + hot) * plb * L + W.batch * (width + 2) * 4
+    kv_read = kv
+    if compact:
+        h2d += cstaged * cplb_all * L + W.batch * (width + 1) * 4
+        kv_read = kv - cstaged * PT * 4096 * L + cstaged * cplb_all * L
     d2h = W.batch * L * 2 * Hkv * D * 2
-    hbm = kv + (staged + hot) * plb * L + d2h
+    hbm = kv_read + (staged + hot) * plb * L + d2h + (cstaged * cplb_all * L if compact else 0)
     return {
         "metric": "decode attention KV GB/s (% of HBM peak) and tokens/s at 262K ctx, 1 GPU",
         "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "data": "synthetic",
+        "dtype": "bf16 + e4m3 (pages not resident)" if compact else "bf16",
         "config": {"workload": "live pool: 4 requests of ~31,744 tokens growing by one token per "
                                "step, 16 layers, histories in pinned host memory (contiguous per "
                                "layer), device pool of 1,491 pages (3/4 of the histories' pages), "
-                               "tile 8192 / split 2048, 2 staging buffers",
+                               + ("every page not resident staged compact (E4M3 codes + FP32 block "
+                                  "scales), exact and compact runs with 2,048-token tiles in one "
+                                  "launch, 2 staging buffers of each kind; value counts every "
+                                  "token at its bf16 size"
+                                  if compact else "tile 8192 / split 2048, 2 staging buffers"),
                    "pool_pages": sc["pool_pages"], "history_pages": Ph},
         "tokens_per_s": round(W.batch / (ms * 1e-3), 2),
         "schedule_equals_resident_bitwise": ok,
         "schedule_page_sources": kinds,
         "per_step": {"staged_pages_per_layer": staged, "copied_in_pages": hot,
+                     "compact_staged_pages_per_layer": cstaged,
                      "host_to_device_bytes": int(h2d), "device_to_host_bytes": int(d2h),
-                     "hbm_bytes": int(hbm), "kv_bytes_read": int(kv)},
+                     "hbm_bytes": int(hbm), "kv_bytes_read": int(kv_read)},
         "roofline": {"bound": "host-to-device", "achieved": round(h2d / (ms * 1e-3) / 1e9, 2),
                      "peak": round(ceiling, 2), "unit": "GB/s",
                      "frac": round(h2d / (ms * 1e-3) / 1e9 / ceiling, 4),
