@@ -36,9 +36,10 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
 # scaled by the factor the same counter shows on a plain 1 GiB device copy
 # (FETCH_SIZE reads 0.5x of the bytes a copy must read, WRITE_SIZE 1.0x).
-# Valid only for the kernel source it was measured on.
+# Valid only for the kernel code it was measured on (source_sha256 hashes the
+# code without comments, see code_text).
 PMC_TRAFFIC = {
-    "source_sha256": "0fa0ab04f3cd7fddb50f0e1acbdbd636d5ff8f963f8579608aeaa6c77e15c9c1",
+    "source_sha256": "a950b23bf0cf8c5dcb12f3dc4e9c7c2c5ff553a34187b072a7db2d9568dd4ef2",
     "workload": "long262k", "tile": 4096, "split": 4096,
     "fetch_kib": 524503.3, "fetch_scale": 1048576 / 524300.1,
     "write_kib": 1584.0, "write_scale": 1.0,
@@ -50,7 +51,7 @@ KERNEL_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_mfma.hip", "paged_kv_cache_
 # decode kernel plus the tile finalize launch, FETCH_SIZE and WRITE_SIZE of
 # both dispatches added, calibrated on the plain copy of the same runs.
 PMC_TRAFFIC_CONC = {
-    "source_sha256": "c8042e0d6d5ac821c6861c2fb06930c779770f0a735ca6b9d6b90eda4cbe1522",
+    "source_sha256": "aed1d9749dd54b077c9ebed44cf2c2c2ba450c8451d74ce95a95bd288f412b3e",
     "workload": "conc", "tile": 8192, "split": 2048,
     "fetch_kib": 254293.9 + 845.0, "fetch_scale": 1048576 / 524300.1,
     "write_kib": 1584.4 + 387.0, "write_scale": 1.0,
@@ -69,7 +70,7 @@ PMC_TRAFFIC_MIXED = {
 # The same for the compact kernel on the 262K compact-older workload
 # (COMPACT_LAUNCH), calibrated on the same plain copy in the same runs.
 PMC_TRAFFIC_FP8 = {
-    "source_sha256": "0aaa68522b8ae01a6e34bf64e369341e7503ef6c59920b72e173a3a6910774b4",
+    "source_sha256": "26051ccbf69d5f419e8fa9c0320be1a6b824a4573358e9306c72fda63a33c0a0",
     "workload": "long262k", "tile": 4800, "split": 4800,
     "fetch_kib": 230053.1, "fetch_scale": 1048576 / 524299.5,
     "write_kib": 1188.0, "write_scale": 1.0,
@@ -79,7 +80,7 @@ FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_a
 
 # The same for the one-launch kernel of both runs (COMPACT_LAUNCH, "one_launch").
 PMC_TRAFFIC_RUNS = {
-    "source_sha256": "d43d6b6559212bbce94ed3dbb077a15bbe475cb6ac01bd8edb8b0083fb6487bb",
+    "source_sha256": "011204fb636cf51a8966593aa409ca4424a6f58b53c923a6ff6da57d0c1877cf",
     "workload": "long262k", "tile": 4800, "exact_tile": 2048,
     "fetch_kib": 295722.0, "fetch_scale": 1048576 / 524299.5,
     "write_kib": 1584.1, "write_scale": 1.0,
@@ -92,20 +93,49 @@ RUNS_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_runs.hip", "paged_kv_cache_10
 # The same for the merge alone on the merge-stress shape (merge_kernel, 64 x
 # 24 rows x 256 partials), calibrated on the plain copy of the same runs.
 PMC_TRAFFIC_MERGE = {
-    "source_sha256": "ff2d2306ca2f6e7fa835fb38468f931fd63e4b95dab8a1803f0a8109d471ea22",
+    "source_sha256": "e3f12e65f1287392e7c45f3360af71f04782a96851f2b181cbeb6fbaf2965a3a",
     "fetch_kib": 197466.5, "fetch_scale": 1048576 / 524301.2,
     "write_kib": 1584.0, "write_scale": 1.0,
 }
 MERGE_SOURCES = ("paged_kv_cache_10_amd/csrc/merge.hip", "paged_kv_cache_10_amd/csrc/device.h")
 
 
-def sources_sha256(files):
+def code_text(text):
+    """C/C++ source without its comments, whitespace runs collapsed to one
+    space: what the compiler sees, so that a comment edit does not count as
+    a kernel change."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def sources_sha256(files, root=None):
+    """SHA-256 over the code (code_text) of each file, in order; paths are
+    relative to `root` (default: the repository)."""
     import hashlib
     h = hashlib.sha256()
-    root = os.path.dirname(os.path.abspath(__file__))
+    root = root or os.path.dirname(os.path.abspath(__file__))
     for f in files:
-        with open(os.path.join(root, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

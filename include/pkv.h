@@ -3,12 +3,13 @@
  *
  * What it computes.  Exact single-token decode attention over a request's
  * whole paged key/value history (KV-cache engineering page, section "Costing
- * the bus before changing anything": every new token reads every byte of
- * history).  The history is cut into tiles; each tile yields its normalised
- * output and its log-sum-exp, and an FP32 merge weights tile t by
- * exp(lse_t - max lse), sums, divides by the summed weights and reports
- * max + log(sum) as the merged log-sum-exp: softmax over the union of the
- * keys (same page, section "Exact recent pages, compact older pages").
+ * the bus before changing anything": each new token attends the entire
+ * history).  The history is cut into tiles; each tile yields an output
+ * already divided by its own softmax sum, plus the log-sum-exp of its
+ * scores, and an FP32 merge weights tile t by exp(lse_t - max lse), adds
+ * the weighted outputs, divides by the total weight and reports
+ * max + log(total) as the merged log-sum-exp: the softmax of all the keys
+ * at once (same page, section "Exact recent pages, compact older pages").
  *
  * Conventions for every entry point.
  *   - Return value: PKV_OK (0) or a negative PKV_ERR_* code.  No exception
@@ -109,9 +110,9 @@ int pkv_pool_destroy(pkv_pool* pool);
 /* --------------------------------------------------------- compact pool --
  * Older pages kept in a compact representation (KV-cache engineering page,
  * section "Exact recent pages, compact older pages": a request's history is
- * served as runs of two representations; a page is converted once it is
- * fully written in every layer, its CRC computed and the page published;
- * until then it is served exact).  The pages name no format; here:
+ * served as runs of two representations; a page is converted only after
+ * every layer has written all its tokens, then checksummed and published,
+ * and is served exact before that).  The pages name no format; here:
  *   codes   E4M3 (OCP 8-bit float: sign, 4 exponent bits with bias 7,
  *           3 mantissa bits, largest finite 448), one byte per element;
  *   scale   one FP32 per (layer, page, K|V, kv head) block:
@@ -147,8 +148,9 @@ int pkv_pool_format(const pkv_pool* pool, int32_t* format_out);
  * have the same geometry.  dev_src_pages, dev_dst_pages: device int32 [n];
  * dev_crc: device uint32 [n].  An id outside its pool is skipped (nothing is
  * written, its CRC is 0); two entries naming one destination race.  The
- * caller converts only pages fully written in every layer and keeps serving
- * them exact until it has the CRC and switches its tables (publishes).
+ * caller converts a page only once all its tokens exist in every layer and
+ * keeps serving it exact until it has the CRC and switches its tables
+ * (publishes).
  * Queued on `stream` (two launches), no host wait; on a stream of its own it
  * runs beside decode, which never waits for it.
  *
@@ -456,8 +458,8 @@ int pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* dev_table,
  * per request (4,096 bytes at 4 KV heads), stored into the host page by a
  * kernel on the write-back stream (GPU memory management page, "Staging as
  * a lease").  For a bf16 staging pool the host arena must be pinned memory
- * the device can address (hipHostMalloc); create fails otherwise.  A new
- * lease may begin only after the previous one is sealed; a seal must name
+ * the device can address (hipHostMalloc); create fails otherwise.  A lease
+ * is refused while the previous one is still unsealed; a seal must name
  * the open lease.  Stage generations only increase.
  * pkv_stager_retire waits for every sealed lease and returns their count as
  * receipts.  Any HIP failure quarantines the stager: begin and seal are
@@ -620,8 +622,8 @@ int pkv_admit_destroy(pkv_admit* a);
  *
  * Compact older pages in the live pool (KV-cache engineering, sections
  * "Exact recent pages, compact older pages" and "What the hybrid tier
- * buys": once the history is off the card the bus is the bound, and a
- * representation is worth the bytes per token it stops moving).
+ * buys": with the history in host memory the bus sets the pace, so a
+ * representation pays for itself by the bus bytes per token it saves).
  * pkv_live_attach_compact (between steps, once)
  *   cstage        compact (E4M3) pool, same KV heads: its num_layers C is the
  *                 number of compact staging buffers (layer l uses buffer

@@ -10,10 +10,10 @@ the method's arithmetic.
 What it computes (KV-cache engineering page, section "Exact recent pages,
 compact older pages"): single-token decode attention over a request's whole
 key/value history, once in one pass, and once tile by tile where every tile
-yields its own normalised output and log-sum-exp and a merge reweights the
-tiles by exp(lse_t - max lse), divides by the summed weights and reports
-max + log(sum) as the merged log-sum-exp.  The merged result is softmax
-attention over the union of all keys.
+gives an output already divided by its own softmax sum plus the log-sum-exp
+of its scores, and a merge reweights the tiles by exp(lse_t - max lse),
+divides by the total weight and reports max + log(total) as the combined
+log-sum-exp.  The merged result is softmax attention over every key.
 
 The compact representation of older pages (same page and section: runs of
 two representations, a page converted once fully written, with a CRC) is in

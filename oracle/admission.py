@@ -6,22 +6,22 @@ cached or batched beyond what the rules below state, so that each rule can
 be checked against the pages by eye.
 
 Sources, by page and section:
-  * Staging without a stall, "Admission that does arithmetic": the device
-    pool has an explicit size (never automatic).  Each context has a target
-    it holds by right, an optional burst it may borrow while pages are free,
-    and a floor of its sink page plus one.  Each step the engine works out
-    the newest pages a context needs, keeps the sink, and fills the missing
-    pages in this order: one of the context's own pages outside the window,
-    a free page, a page reclaimed within the target, or a page taken by
-    shrinking from the context's oldest page while its tail stays hot.
-    Reclamation goes least recently active first, and within that order
-    takes borrowed pages, then pages above target, then whole idle
-    contexts; when none is left the request is refused.  Changes happen
-    only at step boundaries, and every reclamation is ordered and counted.
-  * GPU memory management, "Pages held by right, borrowed or free": the
-    same target / burst / floor, the newest pages and the sink kept on the
-    device, reclamation least recently active first in a fixed order, each
-    step of it counted.
+  * Staging without a stall, "Admission that does arithmetic": the pool's
+    size is set explicitly by the operator.  A context is entitled to a
+    target number of pages, may borrow up to a burst more while free pages
+    exist, and never drops below a floor (its sink page and one more).  At
+    each step the planner decides which newest pages a context should hold,
+    always including the sink, and sources every missing page in a fixed
+    order: a page the context already holds outside that window, then a
+    free page, then a page reclaimed while the context is under its target,
+    and last its own oldest page moved up so the newest stay resident.
+    Reclamation visits the contexts that were active longest ago first and
+    takes, in turn, borrowed pages, pages over target, and whole idle
+    contexts; if nothing remains the request is refused.  The layout only
+    changes between steps and each reclamation is logged in order.
+  * GPU memory management, "Pages held by right, borrowed or free": the same
+    three limits per context, sink and newest pages resident, reclamation
+    ordered by last activity with every step of it logged.
 
 Readings where the pages leave a step open (each is listed in the design
 notes):

@@ -7,13 +7,13 @@ what each definition below states.
 
 Sources, by page and section:
   * KV-cache engineering page, "Costing the bus before changing anything":
-    the exact path attends every key of the history for every new token.
+    on the exact path each new token attends the entire history.
   * KV-cache engineering page, "Exact recent pages, compact older pages":
-    each tile yields its normalised output and its log-sum-exp; the FP32
-    merge weights partial t by exp(lse_t - max_t lse_t), sums the weighted
-    outputs, divides by the summed weights and reports max + log(sum); the
-    result is softmax over the union of the keys, and separately normalised
-    outputs are never simply averaged.
+    a tile gives an output already divided by its own softmax sum, plus the
+    log-sum-exp of its scores; the FP32 merge weights partial t by
+    exp(lse_t - max_t lse_t), adds the weighted outputs, divides by the total
+    weight and reports max + log(total); the result is the softmax of the
+    whole key set, and plain averaging of the partial outputs is ruled out.
 Readings where the pages are silent (each one is listed in the design notes):
   natural logarithm for the log-sum-exp; the softmax scale is inside the
   scores; q head h reads KV head h // (Hq / Hkv); an empty tile is

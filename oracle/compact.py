@@ -9,10 +9,10 @@ call it).  Plain numpy; no blocking or reordering beyond the definitions.
 Sources, by page and section:
   * KV-cache engineering page, "Exact recent pages, compact older pages":
     a request's history is cut into runs of two representations; a page is
-    converted only once it is completely written in every layer, a CRC is
-    computed and the page published, and until then it is served exact.
+    converted only after every layer has written all its tokens, then
+    checksummed and published, and served exact before that.
   * KV-cache engineering page, "What the hybrid tier buys": a representation
-    is judged by the bytes per token it stops moving.
+    is worth the bus bytes per token it saves.
 The pages name no compact format.  Readings (each one is listed in the
 design notes):
   * format: E4M3 as in the OCP 8-bit floating-point specification: sign,

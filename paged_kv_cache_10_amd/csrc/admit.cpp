@@ -11,7 +11,7 @@
 //
 // Per step, for each active context in the order given, the sink first and
 // then the newest pages downward; a missing page is filled by, in order:
-//   1. one of the context's own pages outside its window (its oldest
+//   1. a page the context already holds outside its window (its oldest
 //      non-sink page below the window, or past the end of a history that
 //      got shorter);
 //   2. the lowest-numbered free page, while the context holds fewer than
@@ -21,7 +21,7 @@
 //      pages above their (possibly lowered) target, then whole idle
 //      contexts; a victim gives its oldest non-sink page;
 //   4. the context's own oldest non-sink page older than the one wanted
-//      (shrinking from the oldest, keeping the tail hot);
+//      (the history gives up its oldest pages so the newest stay resident);
 // and when none of these exists the context is refused for the step if it
 // lacks its sink or floor, else its window simply stays shorter.  Borrowing
 // is a count per context (never above its pages over target); moving a page

@@ -1,6 +1,7 @@
 // Compact pages (KV-cache engineering, section "Exact recent pages, compact
-// older pages": runs of two representations, a page converted once it is
-// fully written in every layer, with a CRC, served exact until then).
+// older pages": runs of two representations; a page is converted only after
+// every layer has written all its tokens, checksummed, and served exact
+// before that).
 //
 // Representation: E4M3 codes (OCP 8-bit float: bias 7, 3 mantissa bits,
 // largest finite 448) with one FP32 scale per (layer, page, K|V, kv head)

@@ -32,7 +32,7 @@
 //
 // With compact pages attached (KV-cache engineering, sections "Exact recent
 // pages, compact older pages" and "What the hybrid tier buys": a
-// representation is judged by the bytes per token it stops moving), a
+// representation is worth the bus bytes per token it saves), a
 // non-resident page whose compact copy the caller has published is staged
 // as E4M3 codes and scales instead of bf16: its entry in the exact table is
 // -1 and it joins a compact run of its own (logical order, every page full).

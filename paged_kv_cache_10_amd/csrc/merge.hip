@@ -1,7 +1,7 @@
 // FP32 log-sum-exp merge of attention partials (KV-cache engineering page,
 // section "Exact recent pages, compact older pages"): partial t is weighted
-// by exp(lse_t - max lse), the weighted outputs are summed and divided by the
-// summed weights, and the merged log-sum-exp is max + log(sum).
+// by exp(lse_t - max lse); the sum of weighted outputs over the total
+// weight is the merged output, max + log(total) the merged log-sum-exp.
 //
 // The merge arithmetic (merge_slots) serves three places:
 //   * the final merge of every slot of a row into one output

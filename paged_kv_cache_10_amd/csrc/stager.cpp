@@ -7,8 +7,8 @@
 // Ordering is on the device: the copy streams wait for the previous readers
 // of the buffer they overwrite and for any write-back still landing in a
 // host page they read, the compute stream waits for the copies, the
-// write-back stream waits for the compute stream's consumer event.  Only the
-// changed tail rows are written back (one token per request), by a kernel
+// write-back stream waits for the compute stream's consumer event.  Nothing
+// but the appended token's rows goes back to the host (one per request), by a kernel
 // that stores them into the pinned host pages.  Each
 // window's copy is split in two halves, one on the caller's copy stream and
 // one on a second copy stream the stager owns (default priority), so that one
@@ -187,8 +187,8 @@ PKV_API int pkv_lease_begin(pkv_stager* st, int32_t layer, const int32_t* host_t
   if (!st || !lease) return fail(PKV_ERR_INVALID_ARG, "stager or lease is NULL");
   if (st->quarantined) return fail(PKV_ERR_QUARANTINED, "stager is quarantined; retire it");
   if (st->open)
-    return pkv::set_error(PKV_ERR_LEASE, "lease %llu is not sealed; a new lease may begin only "
-                          "after the previous one is sealed",
+    return pkv::set_error(PKV_ERR_LEASE, "lease %llu is not sealed; seal it before beginning "
+                          "another",
                           (unsigned long long)st->open_generation);
   if (layer < 0 || layer >= st->host_layers) return fail(PKV_ERR_INVALID_ARG, "layer out of range");
   if (batch < 1 || batch > st->max_batch) return fail(PKV_ERR_INVALID_ARG, "batch outside 1..max_batch");

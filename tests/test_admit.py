@@ -1,6 +1,7 @@
 """Device page admission (pkv_admit_*), on the CPU: per-context target,
-burst and floor; the fill order (own page outside the window, free page,
-reclaim within the target, shrink from the oldest); reclamation least
+burst and floor; the fill order (a page the context holds outside its
+window, then a free page, then reclamation while below target, then its own
+oldest page moving up); reclamation least
 recently active first, borrowed pages before pages above target before whole
 idle contexts, then refusal; every placement counted and logged.  Rules from
 Staging without a stall, section "Admission that does arithmetic", and GPU

@@ -66,3 +66,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert p.returncode != 0
     assert "one GPU" in (p.stdout + p.stderr)
+
+
+def test_code_hash_ignores_comments_but_not_code(tmp_path):
+    """The counters stay valid through a comment edit and are dropped by any
+    change to the code, including inside a string literal."""
+    src = tmp_path / "k.hip"
+    base = 'int f(int x) {  // add one\n  return x + 1; /* done */\n}\nconst char* s = "a // b";\n'
+    variants = {
+        "comment": 'int f(int x) {  // add one to x\n  return x + 1;   /* finished\n */\n}\n'
+                   'const char* s = "a // b";\n',
+        "code": 'int f(int x) {  // add one\n  return x + 2; /* done */\n}\nconst char* s = "a // b";\n',
+        "string": 'int f(int x) {  // add one\n  return x + 1; /* done */\n}\nconst char* s = "a // c";\n',
+    }
+    src.write_text(base)
+    h0 = bench.sources_sha256(["k.hip"], root=str(tmp_path))
+    got = {}
+    for name, text in variants.items():
+        src.write_text(text)
+        got[name] = bench.sources_sha256(["k.hip"], root=str(tmp_path)) == h0
+    assert got == {"comment": True, "code": False, "string": False}

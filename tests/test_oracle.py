@@ -6,7 +6,7 @@ The oracle is checked against things other than itself:
   * library routines: torch's scaled-dot-product attention in float64 and
     scipy's logsumexp,
   * closed forms and invariants: merging any tiling equals one pass (the
-    "softmax over the union of the keys" claim on the KV-cache engineering
+    claim that the merge gives the softmax of the whole key set, on the KV-cache engineering
     page, section "Exact recent pages, compact older pages"), identity merge,
     score shifts, permutations,
   * planted mistakes: each mutant of the oracle below must fail a pin.
