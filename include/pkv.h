@@ -637,10 +637,13 @@ int pkv_admit_destroy(pkv_admit* a);
  *                 64..16384 dividing pt_stride x 64.
  *   dev_cstate    device int32 [max_batch * (pt_stride + 1)], the caller's:
  *                 the compact run's table and lengths.
- * pkv_live_publish / pkv_live_retract (host page ids, between steps): mark
- *   host pages whose compact copy in compact_host is written (the caller
- *   converts a page once it is full in every layer, e.g. with
- *   pkv_compact_convert, and publishes it), or no longer valid.
+ * pkv_live_publish / pkv_live_retract (host page ids): mark host pages
+ *   whose compact copy in compact_host is written (the caller converts a
+ *   page once it is full in every layer, e.g. with pkv_compact_convert from
+ *   its pool page while it is the resident tail, and publishes it), or no
+ *   longer valid.  They take effect at the next pkv_live_step_begin.  The
+ *   caller must not rewrite a page's compact bytes while a queued step may
+ *   still copy them (until the copy stream has passed that step's layers).
  * With compact pages attached, pkv_live_step_begin stages a page that is
  *   not resident, full (all 64 tokens inside the length) and published as
  *   compact: its entry in the composed table is -1 (the exact run masks

@@ -5,7 +5,11 @@
 // and the per-step forms: the table written again from pinned host memory
 // with pkv_page_table_write_async (no host wait, an event recorded after the
 // copy) and decoded with pkv_decode_attention_merged_noalloc (no workspace):
-// the same bits once more.
+// the same bits once more.  Then the live pool: the same histories in
+// pinned host memory, an 8-page device pool, one step whose admission keeps
+// each request's sink and newest pages resident and stages the rest, the
+// last token appended again (same values) and written back: the same bits
+// as the resident merged decode, and the host copy unchanged.
 // Writes its inputs and results to the file named on the command line; the
 // test that runs it compares them with the float64 oracle.
 //
@@ -203,6 +207,88 @@ int main(int argc, char** argv) {
   HIP_OK(hipEventDestroy(copied));
   HIP_OK(hipHostFree(h_table));
   HIP_OK(hipHostFree(h_ctx));
+
+  // the live pool over a pinned host copy of the histories
+  {
+    const int LP = 8, SP = 32;
+    void *larena = nullptr, *sarena = nullptr, *host = nullptr;
+    HIP_OK(hipMalloc(&larena, page_bytes * LP));
+    HIP_OK(hipMalloc(&sarena, page_bytes * SP));
+    HIP_OK(hipHostMalloc(&host, page_bytes * num_pages, hipHostMallocMapped));
+    HIP_OK(hipMemcpy(host, arena, page_bytes * num_pages, hipMemcpyDeviceToHost));
+    pkv_pool *lpool = nullptr, *spool = nullptr;
+    if (int rc = pkv_pool_create(&geom, larena, page_bytes * LP, &lpool))
+      return fail_pkv("pkv_pool_create (live)", rc);
+    if (int rc = pkv_pool_create(&geom, sarena, page_bytes * SP, &spool))
+      return fail_pkv("pkv_pool_create (staging)", rc);
+    int32_t* d_state = nullptr;
+    HIP_OK(hipMalloc(&d_state, sizeof(int32_t) * B * (pt_stride + 2)));
+    hipStream_t s_copy, s_compute, s_back;
+    HIP_OK(hipStreamCreateWithFlags(&s_copy, hipStreamNonBlocking));
+    HIP_OK(hipStreamCreateWithFlags(&s_compute, hipStreamNonBlocking));
+    HIP_OK(hipStreamCreateWithFlags(&s_back, hipStreamNonBlocking));
+    pkv_live* live = nullptr;
+    if (int rc = pkv_live_create(lpool, spool, host, page_bytes * num_pages, B, pt_stride,
+                                 d_state, s_copy, s_compute, s_back, &live))
+      return fail_pkv("pkv_live_create", rc);
+    const int32_t ids[B] = {10, 20, 30};
+    const int32_t target[B] = {3, 2, 3};
+    for (int b = 0; b < B; ++b)
+      if (int rc = pkv_live_add(live, ids[b], target[b], 0)) return fail_pkv("pkv_live_add", rc);
+    const int64_t lengths[B] = {ctx[0], ctx[1], ctx[2]};
+    int32_t status[B];
+    pkv_live_info info;
+    if (int rc = pkv_live_step_begin(live, B, ids, lengths, table.data(), pt_stride, status,
+                                     &info))
+      return fail_pkv("pkv_live_step_begin", rc);
+    for (int b = 0; b < B; ++b)
+      if (status[b] == PKV_ADMIT_REFUSED_STEP) {
+        std::fprintf(stderr, "request %d refused\n", b);
+        return 1;
+      }
+    if (info.staged_pages <= 0 || info.resident_pages > LP) {
+      std::fprintf(stderr, "unexpected step: %lld staged, %d resident\n",
+                   (long long)info.staged_pages, info.resident_pages);
+      return 1;
+    }
+    // the newest token of each request, appended again
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < Hkv; ++g)
+        for (int d = 0; d < D; ++d) {
+          kn[(b * Hkv + g) * D + d] = K[b][((size_t)g * ctx[b] + ctx[b] - 1) * D + d];
+          vn[(b * Hkv + g) * D + d] = V[b][((size_t)g * ctx[b] + ctx[b] - 1) * D + d];
+        }
+    HIP_OK(hipMemcpy(d_k, kn.data(), sizeof(uint16_t) * kn.size(), hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_v, vn.data(), sizeof(uint16_t) * vn.size(), hipMemcpyHostToDevice));
+    if (int rc = pkv_live_layer(live, 0, d_q, d_k, d_v, Hq, TILE, scale, d_po2, d_pl2, SLOTS,
+                                d_out2, d_lse2, d_ws, ws_bytes, &opts))
+      return fail_pkv("pkv_live_layer", rc);
+    HIP_OK(hipStreamSynchronize(s_compute));
+    HIP_OK(hipStreamSynchronize(s_back));
+    HIP_OK(hipMemcpy(out2.data(), d_out2, sizeof(float) * out2.size(), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(lse2.data(), d_lse2, sizeof(float) * lse2.size(), hipMemcpyDeviceToHost));
+    if (std::memcmp(out.data(), out2.data(), 4 * out.size()) ||
+        std::memcmp(lse.data(), lse2.data(), 4 * lse.size())) {
+      std::fprintf(stderr, "the live step differs from the resident merged decode\n");
+      return 1;
+    }
+    std::vector<char> dev_copy(page_bytes * num_pages);
+    HIP_OK(hipMemcpy(dev_copy.data(), arena, dev_copy.size(), hipMemcpyDeviceToHost));
+    if (std::memcmp(dev_copy.data(), host, dev_copy.size())) {
+      std::fprintf(stderr, "the host copy changed\n");
+      return 1;
+    }
+    if (int rc = pkv_live_destroy(live)) return fail_pkv("pkv_live_destroy", rc);
+    pkv_pool_destroy(lpool);
+    pkv_pool_destroy(spool);
+    HIP_OK(hipStreamDestroy(s_copy));
+    HIP_OK(hipStreamDestroy(s_compute));
+    HIP_OK(hipStreamDestroy(s_back));
+    HIP_OK(hipFree(larena));
+    HIP_OK(hipFree(sarena));
+    HIP_OK(hipFree(d_state));
+    HIP_OK(hipHostFree(host));
+  }
 
   FILE* f = std::fopen(argv[1], "wb");
   if (!f) {

@@ -3,7 +3,11 @@ by the package build): pool, page tables, the history written with
 pkv_append_kv, merged decode (checked there against decode + merge, and
 against the asynchronous table write from pinned memory followed by the
 no-allocation merged decode, bit for bit), and the results here against
-the float64 oracle on the inputs the program wrote."""
+the float64 oracle on the inputs the program wrote.  The program also runs
+one live-pool step over a pinned host copy of the histories (sink and
+newest pages resident, the rest staged, the last token appended again and
+written back) and checks it bit for bit against the resident decode and the
+host copy unchanged."""
 
 import os
 import subprocess
