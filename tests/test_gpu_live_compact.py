@@ -210,3 +210,52 @@ def test_live_pool_with_compact_older_pages(gpu):
                              pad_value=NAN16)
     assert torch.equal(host.to(DEV), expect)
     live.destroy()
+
+
+def test_attach_and_layer_refusals(gpu):
+    """Attach refuses a bf16 staging pool, a compact host arena of the wrong
+    size, a compact tile that does not divide the table and a second attach;
+    with compact pages attached, a layer whose slot count is not exact tiles
+    plus compact tiles, or whose split differs from its tile, is refused
+    before anything is queued."""
+    L2, T2, W2 = 2, 1024, 32
+    w = I.Workload("livec-ref", seed=731, ctx_lens=[2000], num_layers=L2, tile_tokens=T2)
+    plb = w.page_layer_bytes
+    host = torch.zeros(W2 * plb * L2 // 2, dtype=torch.int16, pin_memory=True)
+    pool = pkv.Pool(torch.zeros(8 * plb * L2 // 2, dtype=torch.int16, device=DEV), L2, Hkv)
+    spool = pkv.Pool(torch.zeros(2 * W2 * plb // 2, dtype=torch.int16, device=DEV), 2, Hkv)
+    cpb = pkv.compact_page_bytes(L2, Hkv)
+    cstage = pkv.Pool(torch.zeros(2 * W2 * cpb // L2, dtype=torch.uint8, device=DEV), 2, Hkv,
+                      compact=True)
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    live = pkv.Live(pool, spool, host, 1, W2, s0, torch.cuda.current_stream(), s1)
+    chost = torch.zeros(W2 * cpb, dtype=torch.uint8, pin_memory=True)
+    for args, needle in (((spool, chost, 1024), "compact (E4M3) pool"),
+                         ((cstage, chost[:-1], 1024), "compact_host_bytes"),
+                         ((cstage, chost, 96), "compact_tile_tokens"),
+                         ((cstage, chost, 1536), "compact_tile_tokens")):
+        with pytest.raises(pkv.PkvError) as e:
+            live.attach_compact(*args)
+        assert needle in str(e.value), str(e.value)
+    live.attach_compact(cstage, chost, 1024)
+    with pytest.raises(pkv.PkvError) as e:
+        live.attach_compact(cstage, chost, 1024)
+    assert "already attached" in str(e.value)
+    with pytest.raises(pkv.PkvError) as e:
+        live.publish([W2])
+    assert "not a host page" in str(e.value)
+    live.add(1, 4, 0)
+    live.publish(list(range(31)))
+    status, info = live.begin([1], [2000], np.arange(W2, dtype=np.int32)[None])
+    assert info["compact_staged_pages"] == 31 - 3        # all but the sink and the window's two
+    q = step_q(1, 0, 1)
+    kn = torch.zeros((1, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    E2 = W2 * 64 // T2
+    for slots, split, needle in ((E2 + E2 - 1, 0, "num_slots"), (2 * E2, 512, "one split")):
+        got = [torch.empty((1, Hq, slots, D), device=DEV), torch.empty((1, Hq, slots), device=DEV),
+               torch.empty((1, Hq, D), device=DEV), torch.empty((1, Hq), device=DEV)]
+        with pytest.raises(pkv.PkvError) as e:
+            live.layer(0, q, kn, kn, T2, 1 / 16, *got, split_tokens=split)
+        assert needle in str(e.value), str(e.value)
+    torch.cuda.synchronize()
+    live.destroy()
