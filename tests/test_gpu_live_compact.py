@@ -43,13 +43,14 @@ def step_q(step, layer, n):
 def served_values(bits, length, compact_pages):
     """[Hkv, length, D] float64: the history attention sees, the listed
     logical pages replaced by their E4M3 codes times block scale (the
-    oracle's quantiser, one block per page and KV head)."""
+    oracle's quantiser, one block per page and KV head: the compact pages'
+    rows are gathered, whole pages, and quantised block by block)."""
     x = oracle.widen_bf16(bits[:, :length])
-    for lp in compact_pages:
+    if len(compact_pages):
+        rows = (64 * np.asarray(compact_pages)[:, None] + np.arange(64)).ravel()
         for g in range(x.shape[0]):
-            blk = x[g, 64 * lp:64 * lp + 64].astype(np.float32)
-            codes, scale = C.quantize_block(blk)
-            x[g, 64 * lp:64 * lp + 64] = C.dequantize(codes, scale)
+            codes, scales = C.quantize_history(x[g, rows].astype(np.float32))
+            x[g, rows] = C.dequantize_history(codes, scales)
     return x
 
 
@@ -258,4 +259,128 @@ def test_attach_and_layer_refusals(gpu):
             live.layer(0, q, kn, kn, T2, 1 / 16, *got, split_tokens=split)
         assert needle in str(e.value), str(e.value)
     torch.cuda.synchronize()
+    live.destroy()
+
+
+def test_live_pool_compact_at_the_4_request_shape(gpu):
+    """The launch bench.py --live-compact times: four ~31,744-token requests
+    of 16 layers over the 20-step schedule of the live-pool test (targets
+    change, a request pauses), a device pool of 1,491 pages, every full page
+    published compact, exact and compact runs with 2,048-token tiles.  Every
+    step and layer bit-equal to the two runs over resident copies (tables
+    read back) plus one merge; steps 1 and 20 on one layer against the
+    float64 oracle over the history as served."""
+    sc = I.live_schedule(20)
+    W = I.Workload("live", seed=81, ctx_lens=sc["final"], num_layers=16, tile_tokens=8192)
+    L16, PT = W.num_layers, W.page_tokens
+    width = 4 * 8192 // PT
+    T4, CT4 = 2048, 2048
+    E4, C4 = width * PT // T4, width * PT // CT4
+    table = I.draw_page_tables(W, width)                # host page = resident page
+    npg = W.num_pages
+    pb = W.page_layer_bytes * L16
+    resident = torch.full((npg * pb // 2,), NAN16, dtype=torch.int16, device=DEV)
+    start = torch.full_like(resident, NAN16)
+    new_k, new_v = {}, {}
+    for layer in range(L16):
+        for b in range(W.batch):
+            k, v = I.device_kv(W, layer, b, DEV)
+            I.device_scatter(resident, W, layer, b, table[b], k, v, pad_value=NAN16)
+            s0 = sc["start"][b]
+            I.device_scatter(start, W, layer, b, table[b], k[:, :s0], v[:, :s0], pad_value=NAN16)
+            new_k[layer, b] = k[:, s0:].contiguous()
+            new_v[layer, b] = v[:, s0:].contiguous()
+            del k, v
+    host = torch.empty(resident.numel(), dtype=torch.int16, pin_memory=True)
+    host.copy_(start)
+    del start
+    rpool = pkv.Pool(resident, L16, Hkv)
+    cpb = pkv.compact_page_bytes(L16, Hkv)
+    cfull = pkv.Pool(torch.zeros(npg * cpb, dtype=torch.uint8, device=DEV), L16, Hkv,
+                     compact=True)
+    full = np.concatenate([table[b, :c // PT] for b, c in enumerate(sc["final"])]).astype(np.int32)
+    ids = torch.from_numpy(full).to(DEV)
+    pkv.compact_convert(rpool, cfull, ids, ids, torch.zeros(ids.numel(), dtype=torch.int32,
+                                                              device=DEV))
+    torch.cuda.synchronize()
+    chost = torch.empty(cfull.arena.numel(), dtype=torch.uint8, pin_memory=True)
+    chost.copy_(cfull.arena)
+    pool = pkv.Pool(torch.full((sc["pool_pages"] * pb // 2,), NAN16, dtype=torch.int16,
+                               device=DEV), L16, Hkv)
+    spool = pkv.Pool(torch.full((2 * npg * W.page_layer_bytes // 2,), NAN16, dtype=torch.int16,
+                                device=DEV), 2, Hkv)
+    cstage = pkv.Pool(torch.full((2 * npg * cpb // L16,), 0xFF, dtype=torch.uint8, device=DEV),
+                      2, Hkv, compact=True)
+    copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
+    live = pkv.Live(pool, spool, host, W.batch, width, copy_s, torch.cuda.current_stream(), wb_s)
+    live.attach_compact(cstage, chost, CT4)
+    live.publish(full)
+    for c, (t, b) in sc["contexts"].items():
+        live.add(c, t, b)
+    S = E4 + C4
+    staged_compact = 0
+    for s, st in enumerate(sc["steps"], 1):
+        for c, (t, b) in st["set_target"].items():
+            live.set_target(c, t, b)
+        ids_s, lens = st["ids"], st["lengths"]
+        n = len(ids_s)
+        status, info = live.begin(ids_s, lens, table[ids_s])
+        assert "refused" not in status
+        staged_compact += info["compact_staged_pages"]
+        comp = live.table(n)[0].cpu().numpy()
+        clen = live.compact_table(n)[1].cpu().numpy()
+        ref_e = table[ids_s].copy()
+        ref_c = np.full((n, width), -1, np.int32)
+        lps = {}
+        for i, ln in enumerate(lens):
+            need = -(-ln // PT)
+            lp = np.nonzero(comp[i, :need] == -1)[0]
+            lps[ids_s[i]] = lp
+            assert clen[i] == PT * lp.size
+            ref_e[i, lp] = -1
+            ref_c[i, :lp.size] = table[ids_s[i], lp]
+        dev_e, dev_c = torch.from_numpy(ref_e).to(DEV), torch.from_numpy(ref_c).to(DEV)
+        dev_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        dev_clen = torch.from_numpy(clen.astype(np.int32)).to(DEV)
+        for layer in range(L16):
+            w_q = I.Workload("live-q", seed=81 + 1000 * s, ctx_lens=[1] * 4, num_layers=16,
+                             tile_tokens=8192)
+            q = I.device_q(w_q, layer, DEV)[ids_s].contiguous()
+            kn = torch.stack([new_k[layer, c][:, lens[i] - 1 - sc["start"][c]]
+                              for i, c in enumerate(ids_s)]).contiguous()
+            vn = torch.stack([new_v[layer, c][:, lens[i] - 1 - sc["start"][c]]
+                              for i, c in enumerate(ids_s)]).contiguous()
+            got = [torch.full((n, Hq, S, D), float("nan"), device=DEV),
+                   torch.full((n, Hq, S), float("nan"), device=DEV),
+                   torch.full((n, Hq, D), float("nan"), device=DEV),
+                   torch.full((n, Hq), float("nan"), device=DEV)]
+            live.layer(layer, q, kn, vn, T4, W.scale, *got)
+            ref = [torch.full_like(x, float("nan")) for x in got]
+            pkv.decode_attention_runs(layer, q, [(rpool, dev_e, dev_len, E4 * T4, T4, 0),
+                                                 (cfull, dev_c, dev_clen, C4 * CT4, CT4, E4)],
+                                      W.scale, ref[0], ref[1])
+            pkv.merge_partials(ref[0], ref[1], ref[2], ref[3])
+            torch.cuda.synchronize()
+            for x, y in zip(got, ref):
+                assert same_bits(x, y), (s, layer)
+            if s in (1, 20) and layer == 9:
+                qf = oracle.widen_bf16(q.view(torch.int16).cpu().numpy().view(np.uint16))
+                for i, c in enumerate(ids_s):
+                    k, v = I.device_kv(W, layer, c, DEV)
+                    kb = k.view(torch.int16).cpu().numpy().view(np.uint16)
+                    vb = v.view(torch.int16).cpu().numpy().view(np.uint16)
+                    kf = served_values(kb, lens[i], lps[c])
+                    vf = served_values(vb, lens[i], lps[c])
+                    eo, el = oracle.decode_one_pass(qf[i], kf, vf, lens[i], W.scale, Hkv)
+                    assert_out_close(got[2][i].cpu().numpy(), eo, what=f"step {s} ctx {c} out")
+                    assert_lse_close(got[3][i].cpu().numpy(), el, what=f"step {s} ctx {c} lse")
+        print(f"step {s}: {status} {info}", flush=True)
+    torch.cuda.synchronize()
+    assert staged_compact > 0
+    expect = torch.full_like(resident, NAN16)
+    for layer in range(L16):
+        for b in range(W.batch):
+            k, v = I.device_kv(W, layer, b, DEV)
+            I.device_scatter(expect, W, layer, b, table[b], k, v, pad_value=NAN16)
+    assert torch.equal(host.to(DEV), expect)
     live.destroy()
