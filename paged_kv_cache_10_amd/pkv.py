@@ -730,14 +730,14 @@ class Live:
         import torch
         if not compact_host.is_pinned():
             raise ValueError("compact_host must be pinned host memory")
-        self.cstage_pool, self.compact_host = cstage_pool, compact_host
-        self.dev_cstate = torch.full((self.max_batch * (self.pt_stride + 1),), -1,
-                                     dtype=torch.int32, device="cuda")
+        dev_cstate = torch.full((self.max_batch * (self.pt_stride + 1),), -1,
+                                dtype=torch.int32, device="cuda")
         _check(lib().pkv_live_attach_compact(self.handle, cstage_pool.handle,
                                              compact_host.data_ptr(),
                                              compact_host.numel() * compact_host.element_size(),
-                                             int(compact_tile_tokens),
-                                             self.dev_cstate.data_ptr()))
+                                             int(compact_tile_tokens), dev_cstate.data_ptr()))
+        # the runtime now addresses these: keep them alive with it
+        self.cstage_pool, self.compact_host, self.dev_cstate = cstage_pool, compact_host, dev_cstate
         self.compact_tile_tokens = int(compact_tile_tokens)
 
     def publish(self, host_pages):
