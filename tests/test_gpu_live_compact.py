@@ -54,7 +54,10 @@ def served_values(bits, length, compact_pages):
     return x
 
 
-def test_live_pool_with_compact_older_pages(gpu):
+@pytest.mark.parametrize("buffers", [2, 1, 3])
+def test_live_pool_with_compact_older_pages(gpu, buffers):
+    """buffers: staging buffers of each kind (exact and compact); with one,
+    every layer's copies wait for the previous layer's readers of it."""
     start = {"A": 2040, "B": 3100, "C": 900}
     steps = 12
     hist = {h: I.Workload(f"livec-{h}", seed=720 + i, ctx_lens=[n + steps], num_layers=L,
@@ -100,10 +103,10 @@ def test_live_pool_with_compact_older_pages(gpu):
 
     arena = torch.full((12 * plb * L // 2,), NAN16, dtype=torch.int16, device=DEV)
     pool = pkv.Pool(arena, L, Hkv)
-    sarena = torch.full((2 * 64 * plb // 2,), NAN16, dtype=torch.int16, device=DEV)
-    spool = pkv.Pool(sarena, 2, Hkv)
-    carena = torch.full((2 * 96 * cpb // L,), 0xFF, dtype=torch.uint8, device=DEV)
-    cstage = pkv.Pool(carena, 2, Hkv, compact=True)
+    sarena = torch.full((buffers * 64 * plb // 2,), NAN16, dtype=torch.int16, device=DEV)
+    spool = pkv.Pool(sarena, buffers, Hkv)
+    carena = torch.full((buffers * 96 * cpb // L,), 0xFF, dtype=torch.uint8, device=DEV)
+    cstage = pkv.Pool(carena, buffers, Hkv, compact=True)
     assert cstage.num_pages == 96
     copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
     live = pkv.Live(pool, spool, host, 3, WIDTH, copy_s, torch.cuda.current_stream(), wb_s)
