@@ -21,6 +21,9 @@
  *     allocates device memory.  `stream` is a hipStream_t passed as void*
  *     (NULL = the default stream); every kernel of a call is queued on it
  *     in order and the host does not wait for it.
+ *   - Handles (pool, stager, admission, live pool) hold host state without
+ *     locks: calls on one handle from several threads must be serialized
+ *     by the caller.  Calls on different handles are independent.
  *   - bf16 means IEEE binary32's upper 16 bits; all outputs are FP32.
  *   - The log-sum-exp is natural-log and includes the softmax scale:
  *     lse = log sum_j exp(scale * q.k_j).
