@@ -78,7 +78,7 @@ struct pkv_live {
   int32_t max_batch = 0;
   int32_t pt_stride = 0;
   int32_t* dev_state = nullptr;    // [max_batch][pt_stride] table, [max_batch] lengths, positions
-  int32_t* ring = nullptr;         // pinned: kRing copies of dev_state's contents
+  int32_t* ring = nullptr;         // pinned: kRing slots, each dev_state's contents then dev_cstate's
   hipEvent_t ring_ev[kRing] = {};
   bool ring_used[kRing] = {};
   hipStream_t copy = nullptr, compute = nullptr, writeback = nullptr;
