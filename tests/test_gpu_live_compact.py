@@ -387,3 +387,147 @@ def test_live_pool_compact_at_the_4_request_shape(gpu):
             I.device_scatter(expect, W, layer, b, table[b], k, v, pad_value=NAN16)
     assert torch.equal(host.to(DEV), expect)
     live.destroy()
+
+
+def test_live_pool_random_schedule(gpu):
+    """A seeded random schedule of 40 steps over six context ids on a
+    20-page pool with compact pages attached: each step a random subset of
+    contexts in random priority order, random target and burst changes,
+    random pages published and retracted, and now and then a context
+    removed and added again under the same id with a new history.  Every
+    step and layer: out, lse and all partials bit-equal to the two runs over
+    resident copies (refused rows empty), the refusal count as reported; at
+    the end the host copy holds exactly the tokens that were served."""
+    rng = np.random.default_rng(20261202)
+    L2, T2, CT2, W2 = 2, 1024, 1024, 48
+    E2, C2 = W2 * 64 // T2, W2 * 64 // CT2
+    NH, grow, steps = 10, 40, 40
+    starts = [int(x) for x in rng.integers(100, 2000, size=NH)]
+    hist = [I.Workload(f"livr-{h}", seed=900 + h, ctx_lens=[starts[h] + grow], num_layers=L2,
+                       tile_tokens=T2) for h in range(NH)]
+    npg = [-(-w.ctx_lens[0] // 64) for w in hist]
+    base = np.concatenate([[0], np.cumsum(npg)[:-1]]).astype(int)
+    Ph = int(sum(npg))
+    plb = hist[0].page_layer_bytes
+    rows = []
+    for h in range(NH):
+        r = np.full(W2, -1, np.int32)
+        r[:npg[h]] = base[h] + np.arange(npg[h])
+        rows.append(r)
+    resident = torch.full((Ph * plb * L2 // 2,), NAN16, dtype=torch.int16, device=DEV)
+    first = torch.full_like(resident, NAN16)
+    kv = {}
+    for h, w in enumerate(hist):
+        for layer in range(L2):
+            k, v = I.device_kv(w, layer, 0, DEV)
+            kv[h, layer] = (k, v)
+            I.device_scatter(resident, w, layer, 0, rows[h], k, v, pad_value=NAN16)
+            I.device_scatter(first, w, layer, 0, rows[h], k[:, :starts[h]], v[:, :starts[h]],
+                             pad_value=NAN16)
+    host = torch.empty(resident.numel(), dtype=torch.int16, pin_memory=True)
+    host.copy_(first)
+    del first
+    rpool = pkv.Pool(resident, L2, Hkv)
+    cpb = pkv.compact_page_bytes(L2, Hkv)
+    cfull = pkv.Pool(torch.zeros(Ph * cpb, dtype=torch.uint8, device=DEV), L2, Hkv, compact=True)
+    full = np.concatenate([base[h] + np.arange(hist[h].ctx_lens[0] // 64)
+                           for h in range(NH)]).astype(np.int32)
+    ids = torch.from_numpy(full).to(DEV)
+    pkv.compact_convert(rpool, cfull, ids, ids, torch.zeros(ids.numel(), dtype=torch.int32,
+                                                              device=DEV))
+    torch.cuda.synchronize()
+    chost = torch.empty(cfull.arena.numel(), dtype=torch.uint8, pin_memory=True)
+    chost.copy_(cfull.arena)
+    pool = pkv.Pool(torch.full((20 * plb * L2 // 2,), NAN16, dtype=torch.int16, device=DEV),
+                    L2, Hkv)
+    spool = pkv.Pool(torch.full((2 * 300 * plb // 2,), NAN16, dtype=torch.int16, device=DEV),
+                     2, Hkv)
+    cstage = pkv.Pool(torch.full((2 * 300 * cpb // L2,), 0xFF, dtype=torch.uint8, device=DEV),
+                      2, Hkv, compact=True)
+    copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
+    live = pkv.Live(pool, spool, host, 6, W2, copy_s, torch.cuda.current_stream(), wb_s)
+    live.attach_compact(cstage, chost, CT2)
+    published = set()
+    ctx_hist = {}
+    next_h = 0
+    for c in range(6):
+        ctx_hist[c] = next_h
+        next_h += 1
+        live.add(c, int(rng.integers(2, 7)), int(rng.integers(0, 3)))
+    length = list(starts)
+    S = E2 + C2
+    refusals = 0
+    for s in range(1, steps + 1):
+        # between steps: targets, publication, re-adds
+        for c in rng.choice(6, size=int(rng.integers(0, 3)), replace=False):
+            live.set_target(int(c), int(rng.integers(2, 9)), int(rng.integers(0, 4)))
+        pick = rng.choice(full, size=int(rng.integers(0, 60)), replace=False)
+        on = [int(p) for p in pick if rng.random() < 0.7]
+        off = [int(p) for p in pick if int(p) not in on]
+        live.publish(on)
+        published.update(on)
+        live.retract(off)
+        published.difference_update(off)
+        if s % 9 == 0 and next_h < NH:
+            c = int(rng.integers(0, 6))
+            live.remove(c)
+            live.add(c, int(rng.integers(2, 7)), int(rng.integers(0, 3)))
+            ctx_hist[c] = next_h
+            next_h += 1
+        active = [int(c) for c in rng.permutation(6)[:int(rng.integers(1, 7))]]
+        hs = [ctx_hist[c] for c in active]
+        lens = [length[h] + 1 for h in hs]
+        n = len(active)
+        status, info = live.begin(active, lens, np.stack([rows[h] for h in hs]))
+        assert info["refused"] == status.count("refused")
+        refusals += info["refused"]
+        comp = live.table(n)[0].cpu().numpy()
+        clen = live.compact_table(n)[1].cpu().numpy()
+        ref_e = np.stack([rows[h] for h in hs]).copy()
+        ref_c = np.full((n, W2), -1, np.int32)
+        rlen = []
+        for i, (h, ln, st) in enumerate(zip(hs, lens, status)):
+            if st == "refused":
+                rlen.append(0)
+                assert clen[i] == 0
+                continue
+            rlen.append(ln)
+            lp = np.nonzero(comp[i, :-(-ln // 64)] == -1)[0]
+            assert all(int(rows[h][p]) in published for p in lp)
+            assert clen[i] == 64 * lp.size
+            ref_e[i, lp] = -1
+            ref_c[i, :lp.size] = rows[h][lp]
+        dev_e, dev_c = torch.from_numpy(ref_e).to(DEV), torch.from_numpy(ref_c).to(DEV)
+        dev_len = torch.tensor(rlen, dtype=torch.int32, device=DEV)
+        dev_clen = torch.from_numpy(clen.astype(np.int32)).to(DEV)
+        for layer in range(L2):
+            q = step_q(s, layer, 6)[:n].contiguous()
+            kn = torch.stack([kv[h, layer][0][:, ln - 1] for h, ln in zip(hs, lens)]).contiguous()
+            vn = torch.stack([kv[h, layer][1][:, ln - 1] for h, ln in zip(hs, lens)]).contiguous()
+            got = [torch.full((n, Hq, S, D), float("nan"), device=DEV),
+                   torch.full((n, Hq, S), float("nan"), device=DEV),
+                   torch.full((n, Hq, D), float("nan"), device=DEV),
+                   torch.full((n, Hq), float("nan"), device=DEV)]
+            live.layer(layer, q, kn, vn, T2, 1 / 16, *got)
+            ref = [torch.full_like(x, float("nan")) for x in got]
+            pkv.decode_attention_runs(layer, q, [(rpool, dev_e, dev_len, E2 * T2, T2, 0),
+                                                 (cfull, dev_c, dev_clen, C2 * CT2, CT2, E2)],
+                                      1 / 16, ref[0], ref[1])
+            pkv.merge_partials(ref[0], ref[1], ref[2], ref[3])
+            torch.cuda.synchronize()
+            for x, y in zip(got, ref):
+                assert same_bits(x, y), (s, layer)
+        for h, ln, st in zip(hs, lens, status):
+            if st != "refused":
+                length[h] = ln
+    torch.cuda.synchronize()
+    print(f"refusals {refusals}, histories used {next_h}", flush=True)
+    assert refusals > 0 and next_h > 6
+    expect = torch.full_like(resident, NAN16)
+    for h, w in enumerate(hist):
+        for layer in range(L2):
+            k, v = kv[h, layer]
+            I.device_scatter(expect, w, layer, 0, rows[h], k[:, :length[h]], v[:, :length[h]],
+                             pad_value=NAN16)
+    assert torch.equal(host.to(DEV), expect)
+    live.destroy()
