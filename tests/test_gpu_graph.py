@@ -6,8 +6,9 @@ with the program's own eager work and synchronisations between replays, must
 give the eager step's bits, and the eager step matches the float64 oracle.
 
 Forms captured: decode + merge per layer (tiles that are splits, and tiles
-finalized from smaller splits), the merged call, per-request tiles + merge,
-and compact + exact runs in one launch + merge."""
+finalized from smaller splits), the merged call with a workspace and the
+one that allocates nothing, per-request tiles + merge, and compact + exact
+runs in one launch + merge."""
 
 import numpy as np
 import pytest
@@ -118,6 +119,37 @@ def test_graph_merged(case):
     for layer in range(LAYERS):
         sep = case.decode(layer, tile=tile, split=split)
         for x, y in zip(sep, (ref[layer], ref[n + layer], ref[2 * n + layer], ref[3 * n + layer])):
+            assert same_bits(x, y)
+
+
+def test_graph_merged_noalloc(case):
+    """The merged call that allocates nothing (split partials in the
+    library's static scratch), captured and replayed: the bits of the
+    workspace form, which the eager step checks against the oracle."""
+    w = case.w
+    tile, split = 1024, 256
+    S = case.num_slots(tile)
+    po, pl, o, l = _buffers(case, S)
+
+    def step():
+        for layer in range(LAYERS):
+            pkv.decode_attention_merged_noalloc(case.pool, layer, case.q[layer], case.dev_table,
+                                                case.dev_ctx, S * tile, tile, w.scale, po[layer],
+                                                pl[layer], o[layer], l[layer], split_tokens=split)
+
+    ref = _capture_and_replay(step, po + pl + o + l)
+    n = LAYERS
+    _check_eager(case, (ref[:n], ref[n:2 * n], ref[2 * n:3 * n], ref[3 * n:]), tile)
+    nb = pkv.decode_workspace_bytes(w.batch, w.num_q_heads, S * tile, tile, w.head_dim, 0, split)
+    ws = torch.zeros(max(nb, 16) // 4 + 4, device=DEV)
+    for layer in range(LAYERS):
+        got = [torch.empty_like(x) for x in (po[layer], pl[layer], o[layer], l[layer])]
+        pkv.decode_attention_merged(case.pool, layer, case.q[layer], case.dev_table, case.dev_ctx,
+                                    S * tile, tile, w.scale, *got, workspace=ws,
+                                    split_tokens=split)
+        torch.cuda.synchronize()
+        for x, y in zip(got, (ref[layer], ref[n + layer], ref[2 * n + layer],
+                              ref[3 * n + layer])):
             assert same_bits(x, y)
 
 
