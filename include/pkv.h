@@ -65,9 +65,10 @@ enum {
   PKV_ERR_PAGE_TABLE = -5,       /* a page-table row the pool cannot serve */
   PKV_ERR_LAUNCH = -6,           /* the HIP runtime refused a launch */
   PKV_ERR_DEVICE = -7,           /* a HIP runtime call (copy, device query) failed */
-  PKV_ERR_LEASE = -8,            /* a lease call out of order (see the stager below) */
+  PKV_ERR_LEASE = -8,            /* a lease or live-pool step call out of order */
   PKV_ERR_BUSY = -9,             /* leases outstanding: retire before destroying */
-  PKV_ERR_QUARANTINED = -10      /* the stager saw a failure; only retire is accepted */
+  PKV_ERR_QUARANTINED = -10      /* a stager or live pool saw a failure: only retire
+                                    (stager) or destroy (live pool) is accepted */
 };
 
 /* Geometry of the arena.  The kernels are built for head_dim = 256,
