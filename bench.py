@@ -284,8 +284,8 @@ def parse():
                     help="also capture the timed step in a HIP graph and time its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true",
-                    help="skip the 4-request, mixed, merge-stress and live-pool lines the "
-                         "default run adds")
+                    help="skip the 4-request, mixed, merge-stress, live-pool and host-staged "
+                         "lines the default run adds")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -1075,15 +1075,17 @@ def merge_traffic():
 
 
 def other_workloads(args):
-    """The 4-request, mixed, merge-stress and live-pool workloads (exact and
-    with compact pages), each measured by a child run of this script (its
-    own process and device memory) with the same step counts: the key
-    figures of each line."""
+    """The 4-request, mixed and merge-stress workloads, the live pool and the
+    262K history staged from host memory (each exact and with compact
+    pages), each measured by a child run of this script (its own process and
+    device memory) with the same step counts: the key figures of each
+    line."""
     import subprocess
     here = os.path.abspath(__file__)
     runs = {"conc": ["--workload", "conc"], "mixed": ["--workload", "mixed"],
             "merge_stress": ["--merge-stress"], "live": ["--live"],
-            "live_compact": ["--live-compact"]}
+            "live_compact": ["--live-compact"], "host_staged": ["--host-staged"],
+            "host_staged_compact": ["--host-staged", "--compact-older"]}
     out = {}
     for name, extra in runs.items():
         cmd = [sys.executable, here, "--no-cpu-baseline", "--no-read-probe", "--no-others",
@@ -1095,11 +1097,10 @@ def other_workloads(args):
             continue
         d = json.loads(lines[-1])
         r = d["roofline"]
-        if r.get("bound") == "host-to-device":        # the live pool: bound by the host bus
+        if r.get("bound") == "host-to-device":        # staged from host memory: the bus
             out[name] = {"workload": d["config"]["workload"], "ms_per_step": d["ms_per_step"],
                          "tokens_per_s": d["tokens_per_s"],
-                         "schedule_equals_resident_bitwise": d["schedule_equals_resident_bitwise"],
-                         "host_to_device_bytes_per_step": d["per_step"]["host_to_device_bytes"],
+                         **{k: v for k, v in d.items() if k.endswith("_bitwise")},
                          "roofline": {k: r.get(k) for k in ("bound", "achieved", "peak", "unit",
                                                             "frac")}}
             continue
