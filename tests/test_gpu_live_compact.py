@@ -331,7 +331,8 @@ def test_live_pool_compact_at_the_4_request_shape(gpu):
         assert "refused" not in status
         staged_compact += info["compact_staged_pages"]
         comp = live.table(n)[0].cpu().numpy()
-        clen = live.compact_table(n)[1].cpu().numpy()
+        clen = (live.compact_table(n)[1].cpu().numpy() if compact
+                else np.zeros(n, dtype=np.int32))
         ref_e = table[ids_s].copy()
         ref_c = np.full((n, width), -1, np.int32)
         lps = {}
@@ -389,9 +390,12 @@ def test_live_pool_compact_at_the_4_request_shape(gpu):
     live.destroy()
 
 
-def test_live_pool_random_schedule(gpu):
+@pytest.mark.parametrize("compact", [True, False])
+def test_live_pool_random_schedule(gpu, compact):
     """A seeded random schedule of 40 steps over six context ids on a
-    20-page pool with compact pages attached: each step a random subset of
+    20-page pool, with compact pages attached or without (then the merged
+    decode over the composed table, 1,024-token tiles of four 256-token
+    splits, against the resident merged decode): each step a random subset of
     contexts in random priority order, random target and burst changes,
     random pages published and retracted, and now and then a context
     removed and added again under the same id with a new history.  Every
@@ -446,7 +450,8 @@ def test_live_pool_random_schedule(gpu):
                       2, Hkv, compact=True)
     copy_s, wb_s = torch.cuda.Stream(), torch.cuda.Stream()
     live = pkv.Live(pool, spool, host, 6, W2, copy_s, torch.cuda.current_stream(), wb_s)
-    live.attach_compact(cstage, chost, CT2)
+    if compact:
+        live.attach_compact(cstage, chost, CT2)
     published = set()
     ctx_hist = {}
     next_h = 0
@@ -455,7 +460,11 @@ def test_live_pool_random_schedule(gpu):
         next_h += 1
         live.add(c, int(rng.integers(2, 7)), int(rng.integers(0, 3)))
     length = list(starts)
-    S = E2 + C2
+    S = E2 + C2 if compact else E2
+    SPLIT2 = 256
+    nbw = pkv.decode_workspace_bytes(6, Hq, E2 * T2, T2, D, 0, SPLIT2)
+    ws = torch.zeros(max(16, nbw) // 4 + 4, device=DEV)
+    ws_ref = torch.zeros_like(ws)
     refusals = 0
     for s in range(1, steps + 1):
         # between steps: targets, publication, re-adds
@@ -464,10 +473,11 @@ def test_live_pool_random_schedule(gpu):
         pick = rng.choice(full, size=int(rng.integers(0, 60)), replace=False)
         on = [int(p) for p in pick if rng.random() < 0.7]
         off = [int(p) for p in pick if int(p) not in on]
-        live.publish(on)
-        published.update(on)
-        live.retract(off)
-        published.difference_update(off)
+        if compact:
+            live.publish(on)
+            published.update(on)
+            live.retract(off)
+            published.difference_update(off)
         if s % 9 == 0 and next_h < NH:
             c = int(rng.integers(0, 6))
             live.remove(c)
@@ -482,7 +492,8 @@ def test_live_pool_random_schedule(gpu):
         assert info["refused"] == status.count("refused")
         refusals += info["refused"]
         comp = live.table(n)[0].cpu().numpy()
-        clen = live.compact_table(n)[1].cpu().numpy()
+        clen = (live.compact_table(n)[1].cpu().numpy() if compact
+                else np.zeros(n, dtype=np.int32))
         ref_e = np.stack([rows[h] for h in hs]).copy()
         ref_c = np.full((n, W2), -1, np.int32)
         rlen = []
@@ -508,12 +519,17 @@ def test_live_pool_random_schedule(gpu):
                    torch.full((n, Hq, S), float("nan"), device=DEV),
                    torch.full((n, Hq, D), float("nan"), device=DEV),
                    torch.full((n, Hq), float("nan"), device=DEV)]
-            live.layer(layer, q, kn, vn, T2, 1 / 16, *got)
             ref = [torch.full_like(x, float("nan")) for x in got]
-            pkv.decode_attention_runs(layer, q, [(rpool, dev_e, dev_len, E2 * T2, T2, 0),
-                                                 (cfull, dev_c, dev_clen, C2 * CT2, CT2, E2)],
-                                      1 / 16, ref[0], ref[1])
-            pkv.merge_partials(ref[0], ref[1], ref[2], ref[3])
+            if compact:
+                live.layer(layer, q, kn, vn, T2, 1 / 16, *got)
+                pkv.decode_attention_runs(layer, q, [(rpool, dev_e, dev_len, E2 * T2, T2, 0),
+                                                     (cfull, dev_c, dev_clen, C2 * CT2, CT2, E2)],
+                                          1 / 16, ref[0], ref[1])
+                pkv.merge_partials(ref[0], ref[1], ref[2], ref[3])
+            else:
+                live.layer(layer, q, kn, vn, T2, 1 / 16, *got, workspace=ws, split_tokens=SPLIT2)
+                pkv.decode_attention_merged(rpool, layer, q, dev_e, dev_len, E2 * T2, T2, 1 / 16,
+                                            *ref, workspace=ws_ref, split_tokens=SPLIT2)
             torch.cuda.synchronize()
             for x, y in zip(got, ref):
                 assert same_bits(x, y), (s, layer)
