@@ -81,9 +81,9 @@ FP8_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_fp8.hip", "paged_kv_cache_10_a
 # The same for the one-launch kernel of both runs (COMPACT_LAUNCH, "one_launch").
 PMC_TRAFFIC_RUNS = {
     "source_sha256": "011204fb636cf51a8966593aa409ca4424a6f58b53c923a6ff6da57d0c1877cf",
-    "workload": "long262k", "tile": 4800, "exact_tile": 2048,
-    "fetch_kib": 295722.0, "fetch_scale": 1048576 / 524299.5,
-    "write_kib": 1584.1, "write_scale": 1.0,
+    "workload": "long262k", "tile": 4800, "exact_tile": 2560,
+    "fetch_kib": 295722.7, "fetch_scale": 1048576 / 524299.5,
+    "write_kib": 1507.5, "write_scale": 1.0,
 }
 RUNS_SOURCES = ("paged_kv_cache_10_amd/csrc/decode_runs.hip", "paged_kv_cache_10_amd/csrc/decode_compact.h",
                 "paged_kv_cache_10_amd/csrc/decode_exact.h", "paged_kv_cache_10_amd/csrc/compact.h",
@@ -234,7 +234,10 @@ LAUNCH = {
 # 2.1-2.5 MB either way).  The full-size compact parity test runs exactly
 # these.
 COMPACT_LAUNCH = {
-    "long262k": dict(exact_tail=32768, tile=4800, split=4800, exact_tile=2048, exact_split=2048,
+    # 192 compact work-groups of 4,800 tokens and 52 exact ones of 2,560 in
+    # one grid (244 of 256 CUs): in a sweep of both tile sizes the fastest
+    # (1.575 ms per step against 1.590 with 2,048-token exact tiles)
+    "long262k": dict(exact_tail=32768, tile=4800, split=4800, exact_tile=2560, exact_split=2560,
                      schedule="one_launch"),
 }
 
