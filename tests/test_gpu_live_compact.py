@@ -331,8 +331,7 @@ def test_live_pool_compact_at_the_4_request_shape(gpu):
         assert "refused" not in status
         staged_compact += info["compact_staged_pages"]
         comp = live.table(n)[0].cpu().numpy()
-        clen = (live.compact_table(n)[1].cpu().numpy() if compact
-                else np.zeros(n, dtype=np.int32))
+        clen = live.compact_table(n)[1].cpu().numpy()
         ref_e = table[ids_s].copy()
         ref_c = np.full((n, width), -1, np.int32)
         lps = {}
